@@ -1,0 +1,162 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) quantized attention forward.
+ *
+ * The path computes the SageAttention-style INT8-QK / FP8-PV attention fixed by
+ * the page "Exact Numerical Contract" (vortex_exact_attention):
+ *   sage_prep      section "Preparation" steps 1-4 (RMSNorm, RoPE, global K
+ *                  mean) and the V maximum of section "V And PV";
+ *   sage_quant_qk  section "Q And K Quantization" (INT8 Q per 32 rows, INT8 K
+ *                  per 64 rows after mean subtraction) and the FP8 V cast of
+ *                  section "V And PV";
+ *   sage_attn_fwd  sections "INT8 QK And Score Domain", "Online Softmax",
+ *                  "V And PV" and "Finalization And Tails".
+ * Inputs follow the page's section "Canonical Boundary": BF16 Q/K/V in NHD
+ * order given as strided views (so the interleaved QKV row of width 21,504 at
+ * offsets 0 / 7,168 / 14,336 is accepted as is); the output is BF16 NHD,
+ * contiguous in (head, dim) so that [N, H*D] is a free reshape.
+ *
+ * Optional rotation: with hadamard = 1, Q and mean-subtracted K rows are
+ * multiplied by the normalized Walsh-Hadamard matrix before INT8
+ * quantization (the NPU issue page on INT8 KV with per-head Hadamard
+ * rotation: the rotation cancels in Q K^T).
+ *
+ * Ownership and threading: the caller allocates every device buffer (sizes
+ * from sage_buffer_sizes) and the workspace.  The library never allocates,
+ * frees or synchronises; it enqueues kernels on the given HIP stream (NULL is
+ * the default stream) and returns.  Calls are reentrant; calls that share
+ * buffers must be ordered by the caller (same stream).  sage_quant_qk must run
+ * after sage_prep on the same buffers and workspace; sage_attn_fwd after
+ * sage_quant_qk.
+ *
+ * Errors: every argument is validated before any launch.  On a refusal the
+ * named status is returned and nothing is written.  A failed launch returns
+ * SAGE_E_HIP.  There is no fallback path.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sage_status {
+    SAGE_OK = 0,
+    SAGE_E_NULL = 1,         /* a required pointer is NULL                              */
+    SAGE_E_SHAPE = 2,        /* B, N, Hq, Hkv or D out of range                         */
+    SAGE_E_STRIDE = 3,       /* unit d stride missing, or output not contiguous in (h,d) */
+    SAGE_E_ALIGN = 4,        /* a row or buffer start is not 16-byte aligned            */
+    SAGE_E_ROPE = 5,         /* rope_dim odd, negative or above D                       */
+    SAGE_E_GQA = 6,          /* Hq is not a multiple of Hkv                             */
+    SAGE_E_WORKSPACE = 7,    /* workspace missing or smaller than sage_buffer_sizes     */
+    SAGE_E_UNSUPPORTED = 8,  /* e.g. hadamard with D = 128, eps not positive            */
+    SAGE_E_HIP = 9           /* a kernel launch failed                                  */
+} sage_status;
+
+/* Problem shape.
+ *   B, N      batch and sequence length (1 <= N <= 2^24)
+ *   Hq, Hkv   query and key/value heads; query head h reads KV head h/(Hq/Hkv)
+ *   D         head dimension, 128 or 256
+ *   rope_dim  R: split-half RoPE rotates dims [0, R) in pairs (i, i + R/2);
+ *             even, 0 <= R <= D (96 for D = 128 on the contract page)
+ *   hadamard  0 or 1 (1 requires D = 256)
+ *   eps       RMSNorm epsilon (1e-5 on the contract page), > 0              */
+typedef struct sage_shape {
+    int32_t B, N, Hq, Hkv, D;
+    int32_t rope_dim;
+    int32_t hadamard;
+    float eps;
+} sage_shape;
+
+/* A read-only BF16 tensor view of logical shape [B, N, H, D].  Element
+ * (b, n, h, d) lives at ptr + 2 * (b*sb + n*sn + h*sh + d*sd) bytes.  sd must
+ * be 1; ptr must be 16-byte aligned and sb, sn, sh multiples of 8 elements. */
+typedef struct sage_view_bf16 {
+    const void *ptr;
+    int64_t sb, sn, sh, sd;
+} sage_view_bf16;
+
+/* Device buffers written by sage_prep / sage_quant_qk and read by
+ * sage_attn_fwd.  Layouts (row-major, sizes from sage_buffer_sizes):
+ *   q8       INT8 [B, Hq, q_rows, D]; rows >= N are zero
+ *   q_scale  FP32 [B, Hq, n_q_groups], n_q_groups = ceil(N/128)*4; scale of
+ *            query rows [32g, 32g+32); groups without a valid row hold 1e-7/127
+ *   k8       INT8 [B, Hkv, k_rows, D], k_rows = 64 * n_k_tiles; rows >= N zero
+ *   k_scale  FP32 [B, Hkv, n_k_tiles], n_k_tiles = ceil(N/64)
+ *   k_mean   FP32 [B, Hkv, D], the global K mean subtracted before quantization
+ *   v8       OCP E4M3 [B, Hkv, n_k_tiles, D, 64]: tile t, channel d holds the
+ *            64 keys of the tile in the order sage_v8_key_of_slot gives; keys
+ *            >= N are zero
+ *   v_scale  FP32 [B, Hkv, D]                                                  */
+typedef struct sage_bufs {
+    int8_t *q8;
+    float *q_scale;
+    int8_t *k8;
+    float *k_scale;
+    float *k_mean;
+    uint8_t *v8;
+    float *v_scale;
+} sage_bufs;
+
+/* Byte sizes of each buffer of sage_bufs and of the workspace, plus the
+ * padded extents of the layouts above. */
+typedef struct sage_sizes {
+    size_t q8, q_scale, k8, k_scale, k_mean, v8, v_scale, workspace;
+    int64_t q_rows, n_q_groups, k_rows, n_k_tiles;
+} sage_sizes;
+
+/* Validates *shape and fills *out.  Returns SAGE_E_NULL / SAGE_E_SHAPE /
+ * SAGE_E_ROPE / SAGE_E_GQA / SAGE_E_UNSUPPORTED on an invalid shape. */
+sage_status sage_buffer_sizes(const sage_shape *shape, sage_sizes *out);
+
+/* Pass 1 ("Preparation" steps 1-4; V maximum of "V And PV").
+ *   q, k, v     BF16 views, Q [B,N,Hq,D], K and V [B,N,Hkv,D] (device memory)
+ *   w_q, w_k    BF16 [D] RMSNorm weights shared by all heads, NULL = ones
+ *   rope_cos/sin BF16 [N, rope_dim/2] (row stride rope_dim/2) coefficients for
+ *               positions 0..N-1; may be NULL when rope_dim == 0
+ *   bufs        k_mean and v_scale are written; q8..v8 untouched
+ *   workspace   device memory of at least sizes.workspace bytes; holds per-tile
+ *               partial sums and maxima that sage_quant_qk reads
+ *   stream      hipStream_t, NULL = default stream
+ * Q is validated but not read here. */
+sage_status sage_prep(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
+                      const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
+                      const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/* Pass 2 ("Q And K Quantization"; FP8 cast of "V And PV").  Same arguments as
+ * sage_prep.  Recomputes RMSNorm + RoPE (+ rotation) bit-identically to pass 1,
+ * subtracts k_mean from K, and writes q8, q_scale, k8, k_scale and v8
+ * (including zero padding rows). */
+sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
+                          const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
+                          const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/* Fused attention ("INT8 QK And Score Domain" through "Finalization And
+ * Tails"): INT8 QK^T on MFMA, base-2 online softmax over the KV tiles in
+ * increasing order, E4M3 P times E4M3 V on MFMA, 1/d normalisation, BF16 out.
+ *   o            BF16 [B, N, Hq, D] output, element (b,n,h,d) at
+ *                o + 2*(b*osb + n*osn + h*osh + d); osh must equal D and osn
+ *                Hq*D (rows reshapeable to [N, Hq*D]); 16-byte aligned.
+ * Only rows n < N are written. */
+sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
+                          int64_t osn, int64_t osh, void *stream);
+
+/* Key (0..63, within its tile) stored at position `slot` (0..63) of every
+ * channel row of a v8 tile; -1 if slot is out of range. */
+int32_t sage_v8_key_of_slot(int32_t slot);
+
+/* Human-readable name of a status code (static string). */
+const char *sage_status_str(sage_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t sage_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H_ */

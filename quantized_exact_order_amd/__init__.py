@@ -1,0 +1,153 @@
+"""MI355X (gfx950) quantized attention forward: Python binding of libsage_amd.
+
+Thin marshalling layer over the C ABI of include/sage.h.  torch is used for
+device memory and streams only; every step of the path (RMSNorm, RoPE, K mean,
+quantization, attention) runs in the library's HIP kernels.
+
+    shape = Shape(B, N, Hq, Hkv, D, rope_dim, hadamard, eps)
+    bufs  = Buffers.allocate(shape, device)
+    prep(shape, bufs, q, k, v, w_q, w_k, cos, sin)       # pass 1
+    quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin)   # pass 2
+    o = attn_fwd(shape, bufs)                            # BF16 [B, N, Hq, D]
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageShape, SageSizes, SageView,
+                   check, lib)
+
+__all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
+           "v8_logical", "v8_slot_keys", "SageError", "LIB_PATH", "EXPORTS"]
+
+
+@dataclass(frozen=True)
+class Shape:
+    B: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    rope_dim: int
+    hadamard: bool = False
+    eps: float = 1e-5
+
+    def c(self) -> SageShape:
+        return SageShape(self.B, self.N, self.Hq, self.Hkv, self.D, self.rope_dim,
+                         int(self.hadamard), self.eps)
+
+
+def buffer_sizes(shape: Shape) -> SageSizes:
+    out = SageSizes()
+    check(lib.sage_buffer_sizes(ctypes.byref(shape.c()), ctypes.byref(out)), "sage_buffer_sizes")
+    return out
+
+
+@dataclass
+class Buffers:
+    """Device tensors behind sage_bufs plus the pass-1 workspace."""
+    q8: torch.Tensor         # int8  [B, Hq, q_rows, D]
+    q_scale: torch.Tensor    # f32   [B, Hq, n_q_groups]
+    k8: torch.Tensor         # int8  [B, Hkv, k_rows, D]
+    k_scale: torch.Tensor    # f32   [B, Hkv, n_k_tiles]
+    k_mean: torch.Tensor     # f32   [B, Hkv, D]
+    v8: torch.Tensor         # uint8 [B, Hkv, n_k_tiles, D, 64] (E4M3, keys in slot order)
+    v_scale: torch.Tensor    # f32   [B, Hkv, D]
+    workspace: torch.Tensor  # uint8 [sizes.workspace]
+
+    @classmethod
+    def allocate(cls, shape: Shape, device) -> "Buffers":
+        z = buffer_sizes(shape)
+        B, Hq, Hkv, D = shape.B, shape.Hq, shape.Hkv, shape.D
+        e = lambda *s, dt: torch.empty(s, dtype=dt, device=device)
+        return cls(e(B, Hq, z.q_rows, D, dt=torch.int8), e(B, Hq, z.n_q_groups, dt=torch.float32),
+                   e(B, Hkv, z.k_rows, D, dt=torch.int8), e(B, Hkv, z.n_k_tiles, dt=torch.float32),
+                   e(B, Hkv, D, dt=torch.float32),
+                   e(B, Hkv, z.n_k_tiles, D, 64, dt=torch.uint8), e(B, Hkv, D, dt=torch.float32),
+                   e(max(int(z.workspace), 1), dt=torch.uint8))
+
+    def c(self) -> SageBufs:
+        return SageBufs(self.q8.data_ptr(), self.q_scale.data_ptr(), self.k8.data_ptr(),
+                        self.k_scale.data_ptr(), self.k_mean.data_ptr(), self.v8.data_ptr(),
+                        self.v_scale.data_ptr())
+
+
+def _view(t: torch.Tensor, name: str) -> SageView:
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a BF16 [B, N, H, D] tensor on the GPU")
+    sb, sn, sh, sd = t.stride()
+    return SageView(t.data_ptr(), sb, sn, sh, sd)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _pass(fn, where, shape, bufs, q, k, v, w_q, w_k, cos, sin, stream):
+    qv, kv, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
+    check(fn(ctypes.byref(shape.c()), ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
+             _ptr(w_q), _ptr(w_k), _ptr(cos), _ptr(sin), ctypes.byref(bufs.c()),
+             bufs.workspace.data_ptr(), bufs.workspace.numel(), _stream(stream)), where)
+
+
+def prep(shape: Shape, bufs: Buffers, q, k, v, w_q=None, w_k=None, cos=None, sin=None, stream=None):
+    """Pass 1: k_mean, v_scale and the workspace partials (sage_prep)."""
+    _pass(lib.sage_prep, "sage_prep", shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+
+
+def quant_qk(shape: Shape, bufs: Buffers, q, k, v, w_q=None, w_k=None, cos=None, sin=None,
+             stream=None):
+    """Pass 2: q8, q_scale, k8, k_scale, v8 (sage_quant_qk)."""
+    _pass(lib.sage_quant_qk, "sage_quant_qk", shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+
+
+def attn_fwd(shape: Shape, bufs: Buffers, o: Optional[torch.Tensor] = None, stream=None):
+    """Fused attention (sage_attn_fwd); returns BF16 [B, N, Hq, D]."""
+    if o is None:
+        o = torch.empty((shape.B, shape.N, shape.Hq, shape.D), dtype=torch.bfloat16,
+                        device=bufs.q8.device)
+    if (o.dtype != torch.bfloat16 or o.dim() != 4 or o.shape[0] != shape.B or o.shape[1] < shape.N
+            or o.shape[2] != shape.Hq or o.shape[3] != shape.D or o.device.type != "cuda"):
+        raise ValueError("o must be a BF16 [B, >=N, Hq, D] tensor on the GPU")
+    sb, sn, sh, sd = o.stride()
+    if sd != 1:
+        raise ValueError("o must have unit stride in d")
+    check(lib.sage_attn_fwd(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), o.data_ptr(),
+                            sb, sn, sh, _stream(stream)), "sage_attn_fwd")
+    return o
+
+
+def forward(q, k, v, w_q=None, w_k=None, cos=None, sin=None, rope_dim: int = 0,
+            hadamard: bool = False, eps: float = 1e-5, stream=None):
+    """All three passes; returns (o, shape, bufs)."""
+    B, N, Hq, D = q.shape
+    shape = Shape(B, N, Hq, k.shape[2], D, rope_dim, hadamard, eps)
+    bufs = Buffers.allocate(shape, q.device)
+    prep(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+    quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+    return attn_fwd(shape, bufs, stream=stream), shape, bufs
+
+
+def v8_slot_keys() -> list:
+    """Key (0..63) stored at each slot of a v8 tile row."""
+    return [lib.sage_v8_key_of_slot(s) for s in range(64)]
+
+
+def v8_logical(shape: Shape, bufs: Buffers) -> torch.Tensor:
+    """v8 rearranged to logical [B, Hkv, N, D] key order (for inspection)."""
+    B, Hkv, nk, D, _ = bufs.v8.shape
+    keys = torch.tensor(v8_slot_keys(), device=bufs.v8.device)
+    inv = torch.empty_like(keys)
+    inv[keys] = torch.arange(64, device=keys.device)
+    t = bufs.v8.index_select(4, inv)                      # [B,Hkv,nk,D,64] in key order
+    return t.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nk * 64, D)[:, :, :shape.N]

@@ -1,0 +1,186 @@
+// api.hip -- host side of the C ABI declared in include/sage.h: argument
+// validation, buffer sizing and kernel launches.  Never allocates, frees or
+// synchronises; every refusal happens before the first launch.
+
+#include "sage.h"
+#include "device.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+sage_status check_shape(const sage_shape *s) {
+    if (!s) return SAGE_E_NULL;
+    if (s->B < 1 || s->N < 1 || s->N > kMaxN || s->Hq < 1 || s->Hkv < 1) return SAGE_E_SHAPE;
+    if (s->D != 128 && s->D != 256) return SAGE_E_SHAPE;
+    if ((int64_t)s->B * s->Hq > 65535 * 64 || s->B > 65535 || s->Hq > 65535) return SAGE_E_SHAPE;
+    if (s->Hq % s->Hkv != 0) return SAGE_E_GQA;
+    if (s->rope_dim < 0 || s->rope_dim > s->D || (s->rope_dim & 1)) return SAGE_E_ROPE;
+    if (s->hadamard != 0 && s->hadamard != 1) return SAGE_E_UNSUPPORTED;
+    if (s->hadamard && s->D != 256) return SAGE_E_UNSUPPORTED;   // exact 1/sqrt(D) needs D = 4^k
+    if (!(s->eps > 0.0f) || !std::isfinite(s->eps)) return SAGE_E_UNSUPPORTED;
+    return SAGE_OK;
+}
+
+void fill_sizes(const sage_shape *s, sage_sizes *z) {
+    const int64_t B = s->B, N = s->N, Hq = s->Hq, Hkv = s->Hkv, D = s->D;
+    z->q_rows = ceil_div(N, 256) * 256;
+    z->n_q_groups = ceil_div(N, 128) * 4;
+    z->n_k_tiles = ceil_div(N, 64);
+    z->k_rows = 64 * z->n_k_tiles;
+    z->q8 = (size_t)(B * Hq * z->q_rows * D);
+    z->q_scale = (size_t)(B * Hq * z->n_q_groups) * 4;
+    z->k8 = (size_t)(B * Hkv * z->k_rows * D);
+    z->k_scale = (size_t)(B * Hkv * z->n_k_tiles) * 4;
+    z->k_mean = (size_t)(B * Hkv * D) * 4;
+    z->v8 = (size_t)(B * Hkv * z->n_k_tiles * D * 64);
+    z->v_scale = (size_t)(B * Hkv * D) * 4;
+    const size_t part = round256((size_t)(B * Hkv * z->n_k_tiles * D) * 4);
+    z->workspace = 2 * part + round256((size_t)(B * Hkv * D) * 4);
+}
+
+sage_status check_view(const sage_view_bf16 *v, int H, const sage_shape *s) {
+    if (!v || !v->ptr) return SAGE_E_NULL;
+    if (v->sd != 1) return SAGE_E_STRIDE;
+    if (v->sb < 0 || v->sn < 0 || v->sh < 0) return SAGE_E_STRIDE;
+    if (!aligned16(v->ptr) || (v->sb & 7) || (v->sn & 7) || (v->sh & 7)) return SAGE_E_ALIGN;
+    (void)H;
+    return SAGE_OK;
+}
+
+sage_status check_bufs(const sage_bufs *b) {
+    if (!b) return SAGE_E_NULL;
+    if (!b->q8 || !b->q_scale || !b->k8 || !b->k_scale || !b->k_mean || !b->v8 || !b->v_scale)
+        return SAGE_E_NULL;
+    const void *all[] = {b->q8, b->q_scale, b->k8, b->k_scale, b->k_mean, b->v8, b->v_scale};
+    for (const void *p : all)
+        if (!aligned16(p)) return SAGE_E_ALIGN;
+    return SAGE_OK;
+}
+
+sage_status build_prep(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
+                       const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
+                       const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,
+                       void *workspace, size_t ws_bytes, sage::PrepParams *p) {
+    sage_status st = check_shape(shape);
+    if (st != SAGE_OK) return st;
+    if ((st = check_view(q, shape->Hq, shape)) != SAGE_OK) return st;
+    if ((st = check_view(k, shape->Hkv, shape)) != SAGE_OK) return st;
+    if ((st = check_view(v, shape->Hkv, shape)) != SAGE_OK) return st;
+    if ((st = check_bufs(bufs)) != SAGE_OK) return st;
+    if (shape->rope_dim > 0 && (!rope_cos || !rope_sin)) return SAGE_E_NULL;
+    if (shape->rope_dim > 0 && (shape->rope_dim / 2) % 8 == 0 && (!aligned16(rope_cos) || !aligned16(rope_sin)))
+        return SAGE_E_ALIGN;
+    if ((w_q && !aligned16(w_q)) || (w_k && !aligned16(w_k))) return SAGE_E_ALIGN;
+    sage_sizes z;
+    fill_sizes(shape, &z);
+    if (!workspace) return SAGE_E_WORKSPACE;
+    if (ws_bytes < z.workspace) return SAGE_E_WORKSPACE;
+    if (!aligned16(workspace)) return SAGE_E_ALIGN;
+
+    std::memset(p, 0, sizeof(*p));
+    p->B = shape->B; p->N = shape->N; p->Hq = shape->Hq; p->Hkv = shape->Hkv; p->D = shape->D;
+    p->R = shape->rope_dim; p->hadamard = shape->hadamard; p->eps = shape->eps;
+    p->q = {static_cast<const uint16_t *>(q->ptr), q->sb, q->sn, q->sh};
+    p->k = {static_cast<const uint16_t *>(k->ptr), k->sb, k->sn, k->sh};
+    p->v = {static_cast<const uint16_t *>(v->ptr), v->sb, v->sn, v->sh};
+    p->w_q = w_q; p->w_k = w_k; p->cos_t = rope_cos; p->sin_t = rope_sin;
+    p->q8 = bufs->q8; p->q_scale = bufs->q_scale; p->k8 = bufs->k8; p->k_scale = bufs->k_scale;
+    p->k_mean = bufs->k_mean; p->v8 = bufs->v8; p->v_scale = bufs->v_scale;
+    const size_t part = round256((size_t)((int64_t)shape->B * shape->Hkv * z.n_k_tiles * shape->D) * 4);
+    char *ws = static_cast<char *>(workspace);
+    p->ws_ksum = reinterpret_cast<float *>(ws);
+    p->ws_vmax = reinterpret_cast<float *>(ws + part);
+    p->ws_vamax = reinterpret_cast<float *>(ws + 2 * part);
+    p->q_rows = z.q_rows; p->k_rows = z.k_rows;
+    p->nq = (int)z.n_q_groups; p->nk = (int)z.n_k_tiles;
+    return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sage_status sage_buffer_sizes(const sage_shape *shape, sage_sizes *out) {
+    if (!out) return SAGE_E_NULL;
+    sage_status st = check_shape(shape);
+    if (st != SAGE_OK) return st;
+    fill_sizes(shape, out);
+    return SAGE_OK;
+}
+
+sage_status sage_prep(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
+                      const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
+                      const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,
+                      void *workspace, size_t ws_bytes, void *stream) {
+    sage::PrepParams p;
+    sage_status st = build_prep(shape, q, k, v, w_q, w_k, rope_cos, rope_sin, bufs, workspace, ws_bytes, &p);
+    if (st != SAGE_OK) return st;
+    return sage_launch_prep_stats(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
+                          const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
+                          const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,
+                          void *workspace, size_t ws_bytes, void *stream) {
+    sage::PrepParams p;
+    sage_status st = build_prep(shape, q, k, v, w_q, w_k, rope_cos, rope_sin, bufs, workspace, ws_bytes, &p);
+    if (st != SAGE_OK) return st;
+    return sage_launch_quant(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
+                          int64_t osn, int64_t osh, void *stream) {
+    sage_status st = check_shape(shape);
+    if (st != SAGE_OK) return st;
+    if ((st = check_bufs(bufs)) != SAGE_OK) return st;
+    if (!o) return SAGE_E_NULL;
+    if (osh != shape->D || osn != (int64_t)shape->Hq * shape->D || osb < 0) return SAGE_E_STRIDE;
+    if (!aligned16(o) || (osb & 7)) return SAGE_E_ALIGN;
+    sage_sizes z;
+    fill_sizes(shape, &z);
+    sage::AttnParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = shape->B; p.N = shape->N; p.Hq = shape->Hq; p.Hkv = shape->Hkv;
+    p.grp = shape->Hq / shape->Hkv;
+    p.nq = (int)z.n_q_groups; p.nk = (int)z.n_k_tiles;
+    p.q_rows = z.q_rows; p.k_rows = z.k_rows;
+    p.c = (float)((1.0 / std::sqrt((double)shape->D)) * 1.4426950408889634073599246810019);
+    p.q8 = bufs->q8; p.q_scale = bufs->q_scale; p.k8 = bufs->k8; p.k_scale = bufs->k_scale;
+    p.v8 = bufs->v8; p.v_scale = bufs->v_scale;
+    p.o = static_cast<uint16_t *>(o);
+    p.osb = osb; p.osn = osn; p.osh = osh;
+    return sage_launch_attn(p, shape->D, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+int32_t sage_v8_key_of_slot(int32_t slot) {
+    if (slot < 0 || slot >= 64) return -1;
+    return sage_v8_slot_key(slot);
+}
+
+const char *sage_status_str(sage_status s) {
+    switch (s) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_E_NULL: return "SAGE_E_NULL: a required pointer is NULL";
+    case SAGE_E_SHAPE: return "SAGE_E_SHAPE: B, N, heads or head dim out of range";
+    case SAGE_E_STRIDE: return "SAGE_E_STRIDE: d stride must be 1 and the output contiguous in (head, dim)";
+    case SAGE_E_ALIGN: return "SAGE_E_ALIGN: buffers and rows must be 16-byte aligned";
+    case SAGE_E_ROPE: return "SAGE_E_ROPE: rope_dim must be even and within [0, D]";
+    case SAGE_E_GQA: return "SAGE_E_GQA: query heads must be a multiple of KV heads";
+    case SAGE_E_WORKSPACE: return "SAGE_E_WORKSPACE: workspace missing or too small";
+    case SAGE_E_UNSUPPORTED: return "SAGE_E_UNSUPPORTED: option not supported for this shape";
+    case SAGE_E_HIP: return "SAGE_E_HIP: a kernel launch failed";
+    }
+    return "unknown sage_status";
+}
+
+int32_t sage_version(void) { return 100; }
+
+}  // extern "C"

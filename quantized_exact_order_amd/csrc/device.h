@@ -1,0 +1,133 @@
+// device.h -- gfx950 device helpers shared by the preparation and attention
+// kernels of this library: number-format conversions, lane exchanges and the
+// parameter blocks the host passes to each kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Number formats.  All conversions that feed a bit-exact output round to
+// nearest-even, as the contract page requires ("round ... to BF16 RN",
+// cvt.rni.sat for INT8, E4M3 RN satfinite).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// Two FP32 values -> packed BF16 pair (lo in bits 0-15), hardware RNE
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 v = {lo, hi};
+    bf2 r = __builtin_convertvector(v, bf2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Value after rounding to BF16 (RNE), as FP32.
+__device__ __forceinline__ float round_bf16(float x) { return bf16_lo(pack_bf16x2(x, 0.0f)); }
+
+// FP32 -> INT8: round to nearest even, saturate to [-128, 127], NaN -> 0.
+__device__ __forceinline__ int32_t to_i8(float x) {
+    float r = rintf(x);                        // v_rndne_f32
+    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+    return (x == x) ? (int32_t)r : 0;
+}
+
+// FP32 -> OCP E4M3 byte, round to nearest even, saturating finite overflow to
+// +-448 and NaN to 0x7F (sign kept).  Integer rounding on the FP32 encoding:
+// normal results keep 3 of the 23 mantissa bits; values below 2^-6 are
+// multiples of 2^-9 and are rounded with v_rndne_f32 after an exact 2^9 scale.
+__device__ __forceinline__ uint32_t to_e4m3(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;
+    if (a >= 0x43e00000u) return sign | 0x7eu;              // |x| >= 448
+    if (a < 0x3c800000u) {                                    // |x| < 2^-6
+        float q = rintf(__uint_as_float(a) * 512.0f);
+        return sign | (uint32_t)q;
+    }
+    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);            // RNE at bit 20
+    uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// ---------------------------------------------------------------------------
+// Lane exchanges (wave64).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = __builtin_fmaxf(v, shfl_xor_f(v, m));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks.
+// ---------------------------------------------------------------------------
+
+struct View {
+    const uint16_t *ptr;
+    int64_t sb, sn, sh;
+};
+
+struct PrepParams {
+    int B, N, Hq, Hkv, D, R, hadamard;
+    float eps;
+    View q, k, v;
+    const uint16_t *w_q, *w_k;          // NULL = unit weights
+    const uint16_t *cos_t, *sin_t;      // [N, R/2]
+    int8_t *q8;
+    float *q_scale;
+    int8_t *k8;
+    float *k_scale;
+    float *k_mean;
+    uint8_t *v8;
+    float *v_scale;
+    float *ws_ksum;                     // [B, Hkv, nk, D] per-tile K column sums
+    float *ws_vmax;                     // [B, Hkv, nk, D] per-tile V column max |v|
+    float *ws_vamax;                    // [B, Hkv, D] floored V channel maximum
+    int64_t q_rows, k_rows;
+    int nq, nk;
+};
+
+struct AttnParams {
+    int B, N, Hq, Hkv, grp, nq, nk;
+    int64_t q_rows, k_rows;
+    float c;                            // (1/sqrt(D)) * log2(e), FP32
+    const int8_t *q8;
+    const float *q_scale;
+    const int8_t *k8;
+    const float *k_scale;
+    const uint8_t *v8;
+    const float *v_scale;
+    uint16_t *o;
+    int64_t osb, osn, osh;
+};
+
+}  // namespace sage
+
+// Host-side launchers (defined in prep.hip / attn.hip); return hipGetLastError().
+hipError_t sage_launch_prep_stats(const sage::PrepParams &p, hipStream_t s);
+hipError_t sage_launch_quant(const sage::PrepParams &p, hipStream_t s);
+hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s);
+
+// In-tile key order of a v8 tile row: slot -> key (both 0..63).
+__host__ __device__ __forceinline__ int sage_v8_slot_key(int slot) {
+    // slot = 32*h + 16*c + r  <->  key = 32*c + 8*(r/4) + 4*h + r%4 : the key
+    // that the INT8 QK accumulator register r of block c holds in lane half h.
+    int h = slot >> 5, c = (slot >> 4) & 1, r = slot & 15;
+    return 32 * c + 8 * (r >> 2) + 4 * h + (r & 3);
+}

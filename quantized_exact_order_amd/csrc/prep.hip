@@ -1,0 +1,465 @@
+// prep.hip -- preparation kernels for gfx950: per-head RMSNorm and split-half
+// RoPE of Q and K, the global K mean, INT8 quantization of Q and mean-smoothed
+// K, and the per-channel FP8 (OCP E4M3) cast of V.
+//
+// Follows the page "Exact Numerical Contract", sections "Preparation",
+// "Q And K Quantization" and "V And PV".  Every output of these kernels is a
+// bit-exact target, so every rounding below is fixed:
+//   * RMSNorm: sum of squares as a balanced pairwise tree over d in natural
+//     order (8 elements per lane, then xor-butterflies over the lanes of the
+//     row, which is the same tree), inv = 1/sqrt(ss/D + eps) with IEEE
+//     division and square root, y = bf16((x*inv)*w);
+//   * RoPE: z_i = bf16(a*c - b*s), z_{i+R/2} = bf16(b*c + a*s) on BF16 y and
+//     BF16 coefficients (products exact in FP32);
+//   * K mean: pairwise tree over the sequence padded with +0 to a power of two
+//     (>= 64): an in-tile tree over 64 rows here, a tree over tiles in
+//     prep_reduce_kernel;
+//   * quantization: amax = max(1e-7, max|u|), scale = amax/127,
+//     q = rni_sat(u * (127/amax)); V: v_scale = amax/2.25,
+//     v8 = e4m3_rn_satfinite(v * (2.25/amax)).
+// The file is built with -ffp-contract=off: no multiply-add is fused.
+//
+// HBM-bound: each kernel streams its rows once with 16-byte loads (one row
+// of D BF16 values is D/8 lanes), keeps per-row work in registers and uses LDS
+// only for the RoPE partner exchange and the 64-row column reductions.
+
+#include "device.h"
+
+namespace sage {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Loads 8 consecutive BF16 values (16 bytes) of row (b, n, h) starting at
+// element 8*j; zeros when the row is invalid.
+__device__ __forceinline__ uint4 load_row8(const View &v, int b, int n, int h, int j, bool valid) {
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (valid) {
+        const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)n * v.sn + (int64_t)h * v.sh + 8 * j;
+        r = *reinterpret_cast<const uint4 *>(p);
+    }
+    return r;
+}
+
+__device__ __forceinline__ void unpack8(uint4 r, float x[8]) {
+    x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x);
+    x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
+    x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z);
+    x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float y[8]) {
+    return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                      pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+}
+
+// RMSNorm of one row held by L consecutive lanes (8 elements each).  Every
+// lane of the wave must call this (lane exchanges).  Result rounded to BF16.
+template <int L>
+__device__ __forceinline__ void rmsnorm8(const float x[8], const uint16_t *w, int j, float eps,
+                                         int D, float y[8]) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = x[i] * x[i];
+    float a0 = t[0] + t[1], a1 = t[2] + t[3], a2 = t[4] + t[5], a3 = t[6] + t[7];
+    float b0 = a0 + a1, b1 = a2 + a3;
+    float ss = b0 + b1;
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) ss = ss + shfl_xor_f(ss, m);
+    float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    float wv[8];
+    if (w) {
+        unpack8(*reinterpret_cast<const uint4 *>(w + 8 * j), wv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float n1 = x[i] * inv;
+        float n2 = n1 * wv[i];
+        y[i] = round_bf16(n2);
+    }
+}
+
+// Split-half RoPE of the 8 elements [8j, 8j+8) of row `r` whose normalized
+// values (BF16) sit in LDS row `yrow`; n is the position.
+__device__ __forceinline__ void rope8(const uint16_t *yrow, int j, int n, int R,
+                                      const uint16_t *cos_t, const uint16_t *sin_t, float z[8]) {
+    const int half = R >> 1;
+    const int d0 = 8 * j;
+    float y[8];
+    unpack8(*reinterpret_cast<const uint4 *>(yrow + d0), y);
+    if (d0 >= R) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = y[i];
+        return;
+    }
+    if ((half & 7) == 0) {
+        // whole 8-element blocks pair up: block j with block j +- half/8
+        const bool lower = d0 < half;
+        const int pd = lower ? d0 + half : d0 - half;     // partner block start
+        const int cd = lower ? d0 : pd;                   // coefficient index
+        float pv[8], c[8], s[8];
+        unpack8(*reinterpret_cast<const uint4 *>(yrow + pd), pv);
+        unpack8(*reinterpret_cast<const uint4 *>(cos_t + (int64_t)n * half + cd), c);
+        unpack8(*reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd), s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r;
+            if (lower) r = y[i] * c[i] - pv[i] * s[i];     // a*c - b*s
+            else r = y[i] * c[i] + pv[i] * s[i];           // b*c + a*s
+            z[i] = round_bf16(r);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int d = d0 + i;
+        float r;
+        if (d < half) {
+            float a = y[i], b = __uint_as_float((uint32_t)yrow[d + half] << 16);
+            float c = __uint_as_float((uint32_t)cos_t[(int64_t)n * half + d] << 16);
+            float s = __uint_as_float((uint32_t)sin_t[(int64_t)n * half + d] << 16);
+            r = round_bf16(a * c - b * s);
+        } else if (d < R) {
+            float b = y[i], a = __uint_as_float((uint32_t)yrow[d - half] << 16);
+            float c = __uint_as_float((uint32_t)cos_t[(int64_t)n * half + d - half] << 16);
+            float s = __uint_as_float((uint32_t)sin_t[(int64_t)n * half + d - half] << 16);
+            r = round_bf16(b * c + a * s);
+        } else {
+            r = y[i];
+        }
+        z[i] = r;
+    }
+}
+
+// Normalized Walsh-Hadamard transform of a row held by L lanes (8 consecutive
+// elements each), in place, FP32.  Butterfly spans 1, 2, 4 inside the lane,
+// then 8 .. 4L across lanes; pair (a at i, b at i+span) -> (a+b, a-b); finally
+// times 1/sqrt(8L) (1/16 for the supported 256-wide rows, exact).
+template <int L>
+__device__ __forceinline__ void wht8(float u[8], int j) {
+#pragma unroll
+    for (int span = 1; span < 8; span <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & span) == 0) {
+                float a = u[i], b = u[i + span];
+                u[i] = a + b;
+                u[i + span] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int lm = 1; lm < L; lm <<= 1) {
+        const bool upper = (j & lm) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float other = shfl_xor_f(u[i], lm);
+            u[i] = upper ? (other - u[i]) : (u[i] + other);
+        }
+    }
+    const float s = (L == 32) ? 0.0625f : 1.0f / sqrtf((float)(8 * L));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = u[i] * s;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: K rows -> per-tile column sums (pairwise over 64 rows); V rows ->
+// per-tile column maxima of |v|.  Grid (nk, Hkv, B), 256 threads.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p) {
+    constexpr int L = D / 8;               // lanes per row
+    constexpr int RPP = kThreads / L;      // rows per pass
+    constexpr int NPASS = 64 / RPP;
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t zbuf[64 * D];
+    // V partial maxima reuse ybuf once the RoPE pass has consumed it
+    float *vpart = reinterpret_cast<float *>(ybuf);
+    static_assert(RPP * D * sizeof(float) <= sizeof(ybuf), "vpart must fit in ybuf");
+
+    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, j = tid % L, rr = tid / L;
+
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        float x[8], y[8];
+        unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
+        rmsnorm8<L>(x, p.w_k, j, p.eps, D, y);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = pack8(y);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        float z[8];
+        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, z);
+        if (n >= p.N) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z[i] = 0.0f;       // padding leaves are +0
+        }
+        *reinterpret_cast<uint4 *>(&zbuf[r * D + 8 * j]) = pack8(z);
+    }
+    // V: running max |v| of this thread's 8 channels over its rows
+    float vm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vm[i] = 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        float x[8];
+        unpack8(load_row8(p.v, b, n, h, j, n < p.N), x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vm[i] = __builtin_fmaxf(vm[i], __builtin_fabsf(x[i]));
+    }
+    __syncthreads();                       // every RoPE read of ybuf is done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vpart[rr * D + 8 * j + i] = vm[i];
+    __syncthreads();
+
+    const int64_t wsoff = (((int64_t)b * p.Hkv + h) * p.nk + t) * D;
+    for (int d = tid; d < D; d += kThreads) {
+        float v[64];
+#pragma unroll
+        for (int r = 0; r < 64; ++r) v[r] = __uint_as_float((uint32_t)zbuf[r * D + d] << 16);
+#pragma unroll
+        for (int w = 64; w > 1; w >>= 1) {
+#pragma unroll
+            for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+        }
+        p.ws_ksum[wsoff + d] = v[0];
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) m = __builtin_fmaxf(m, vpart[r * D + d]);
+        p.ws_vmax[wsoff + d] = m;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1b: per (b, h, d) the pairwise tree over the tile sums (padded with +0
+// to a power of two), mean = S/N; V channel maximum over tiles, floored at
+// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv), D threads.
+// ---------------------------------------------------------------------------
+__global__ void prep_reduce_kernel(const PrepParams p) {
+    const int bh = blockIdx.x, d = threadIdx.x, D = p.D;
+    const int nk = p.nk;
+    const float *ks = p.ws_ksum + (int64_t)bh * nk * D + d;
+    const float *vm = p.ws_vmax + (int64_t)bh * nk * D + d;
+    int P = 1;
+    while (P < nk) P <<= 1;
+    // Streaming evaluation of the balanced tree: after leaf i, merge the
+    // completed subtrees (ctz(i+1) merges); left subtree + right subtree.
+    float stack[32];
+    int top = 0;
+    for (int i = 0; i < P; ++i) {
+        float x = (i < nk) ? ks[(int64_t)i * D] : 0.0f;
+        for (int m = __builtin_ctz((unsigned)(i + 1)); m > 0; --m) x = stack[--top] + x;
+        stack[top++] = x;
+    }
+    p.k_mean[(int64_t)bh * D + d] = stack[0] / (float)p.N;
+    float m = 0.0f;
+    for (int i = 0; i < nk; ++i) m = __builtin_fmaxf(m, vm[(int64_t)i * D]);
+    const float amax = (m > 1e-7f) ? m : 1e-7f;
+    p.v_scale[(int64_t)bh * D + d] = amax / 2.25f;
+    p.ws_vamax[(int64_t)bh * D + d] = amax;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2a: Q -> INT8, one scale per 32 rows.  Grid (q_rows/128, Hq, B); wave w
+// of block x owns group g = 4x + w (rows [32g, 32g+32)).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
+    constexpr int L = D / 8;
+    constexpr int RPW = 64 / L;            // rows per wave pass
+    constexpr int NP = 32 / RPW;
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[4][32 * D];
+
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane % L, rr = lane / L;
+    const int g = blockIdx.x * 4 + wave;
+    uint16_t *yb = ybuf[wave];
+
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int r = pass * RPW + rr, n = 32 * g + r;
+        float x[8], y[8];
+        unpack8(load_row8(p.q, b, n, h, j, n < p.N), x);
+        rmsnorm8<L>(x, p.w_q, j, p.eps, D, y);
+        *reinterpret_cast<uint4 *>(&yb[r * D + 8 * j]) = pack8(y);
+    }
+    __syncthreads();
+    float u[NP][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int r = pass * RPW + rr, n = 32 * g + r;
+        rope8(&yb[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, u[pass]);
+        if (p.hadamard) wht8<L>(u[pass], j);
+        if (n < p.N) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(u[pass][i]));
+        }
+    }
+    amax = wave_max_f(amax);
+    amax = (amax > 1e-7f) ? amax : 1e-7f;
+    const float scale = amax / 127.0f;
+    const float mul = 127.0f / amax;
+    int8_t *dst = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + 32 * g) * D;
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int r = pass * RPW + rr, n = 32 * g + r;
+        uint32_t lo = 0, hi = 0;
+        if (n < p.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lo |= (uint32_t)(to_i8(u[pass][i] * mul) & 0xff) << (8 * i);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hi |= (uint32_t)(to_i8(u[pass][4 + i] * mul) & 0xff) << (8 * i);
+        }
+        *reinterpret_cast<uint2 *>(dst + (int64_t)r * D + 8 * j) = make_uint2(lo, hi);
+    }
+    if (lane == 0 && g < p.nq) p.q_scale[((int64_t)b * p.Hq + h) * p.nq + g] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2b: K -> subtract k_mean -> INT8, one scale per 64-row tile.
+// Grid (nk, Hkv, B).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
+    constexpr int L = D / 8;
+    constexpr int RPP = kThreads / L;
+    constexpr int NPASS = 64 / RPP;
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[64 * D];
+    __shared__ float wmax[kThreads / 64];
+
+    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, j = tid % L, rr = tid / L;
+
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        float x[8], y[8];
+        unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
+        rmsnorm8<L>(x, p.w_k, j, p.eps, D, y);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = pack8(y);
+    }
+    __syncthreads();
+    const float *mu = p.k_mean + ((int64_t)b * p.Hkv + h) * D + 8 * j;
+    float mean[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = mu[i];
+    float u[NPASS][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        float z[8];
+        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, z);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[pass][i] = z[i] - mean[i];
+        if (p.hadamard) wht8<L>(u[pass], j);
+        if (n < p.N) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(u[pass][i]));
+        }
+    }
+    amax = wave_max_f(amax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    amax = (amax > 1e-7f) ? amax : 1e-7f;
+    const float scale = amax / 127.0f;
+    const float mul = 127.0f / amax;
+    int8_t *dst = p.k8 + (((int64_t)b * p.Hkv + h) * p.k_rows + 64 * t) * D;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        uint32_t lo = 0, hi = 0;
+        if (n < p.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lo |= (uint32_t)(to_i8(u[pass][i] * mul) & 0xff) << (8 * i);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hi |= (uint32_t)(to_i8(u[pass][4 + i] * mul) & 0xff) << (8 * i);
+        }
+        *reinterpret_cast<uint2 *>(dst + (int64_t)r * D + 8 * j) = make_uint2(lo, hi);
+    }
+    if (tid == 0) p.k_scale[((int64_t)b * p.Hkv + h) * p.nk + t] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2c: V -> E4M3 into tiles [D][64], keys of a tile in the slot order of
+// sage_v8_slot_key (the key order in which the attention kernel holds its
+// probabilities).  Grid (nk, Hkv, B).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
+    constexpr int L = D / 8;
+    constexpr int RPP = kThreads / L;
+    constexpr int NPASS = 64 / RPP;
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[64 * D];
+
+    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, j = tid % L, rr = tid / L;
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr, n = t * 64 + r;
+        *reinterpret_cast<uint4 *>(&vbuf[r * D + 8 * j]) = load_row8(p.v, b, n, h, j, n < p.N);
+    }
+    __syncthreads();
+    const float *amax = p.ws_vamax + ((int64_t)b * p.Hkv + h) * D;
+    uint8_t *dst = p.v8 + (((int64_t)b * p.Hkv + h) * p.nk + t) * (int64_t)D * 64;
+    for (int e = tid; e < 2 * D; e += kThreads) {
+        const int d = e >> 1, half = e & 1;
+        const float mul = 2.25f / amax[d];
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = sage_v8_slot_key(32 * half + 4 * k + i);
+                const float x = __uint_as_float((uint32_t)vbuf[key * D + d] << 16);
+                word |= to_e4m3(x * mul) << (8 * i);
+            }
+            w[k] = word;
+        }
+        uint4 *o = reinterpret_cast<uint4 *>(dst + (int64_t)d * 64 + 32 * half);
+        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+}  // namespace
+}  // namespace sage
+
+using sage::PrepParams;
+
+hipError_t sage_launch_prep_stats(const PrepParams &p, hipStream_t s) {
+    dim3 grid(p.nk, p.Hkv, p.B);
+    if (p.D == 128) sage::prep_stats_kernel<128><<<grid, sage::kThreads, 0, s>>>(p);
+    else sage::prep_stats_kernel<256><<<grid, sage::kThreads, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv), dim3(p.D), 0, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t sage_launch_quant(const PrepParams &p, hipStream_t s) {
+    dim3 gq((unsigned)(p.q_rows / 128), p.Hq, p.B);
+    dim3 gk(p.nk, p.Hkv, p.B);
+    if (p.D == 128) {
+        sage::quant_q_kernel<128><<<gq, sage::kThreads, 0, s>>>(p);
+        sage::quant_k_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
+        sage::quant_v_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
+    } else {
+        sage::quant_q_kernel<256><<<gq, sage::kThreads, 0, s>>>(p);
+        sage::quant_k_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
+        sage::quant_v_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
+    }
+    return hipGetLastError();
+}

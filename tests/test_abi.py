@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every function include/sage.h declares,
+sizes buffers, and refuses invalid arguments by name before any launch.
+Host-only: no test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sage_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def sage():
+    import quantized_exact_order_amd as sage
+    return sage
+
+
+def test_library_exports_every_declared_symbol(sage):
+    names = _declared_functions()
+    assert set(names) == set(sage.EXPORTS), names
+    raw = ctypes.CDLL(sage.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(sage):
+    from quantized_exact_order_amd._lib import lib, STATUS_NAMES
+    assert lib.sage_version() >= 100
+    for code, name in STATUS_NAMES.items():
+        assert lib.sage_status_str(code).decode().startswith(name)
+
+
+def test_buffer_sizes_canonical(sage):
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "canonical_boundary.json")))
+    z = sage.buffer_sizes(sage.Shape(1, 37810, 56, 56, 128, 96))
+    assert z.n_q_groups == gold["q_scale_shape"][2]
+    assert z.n_k_tiles == gold["k_scale_shape"][2]
+    assert z.k_rows == gold["v_padded_rows"]
+    assert z.q_scale == 56 * 1184 * 4 and z.k_scale == 56 * 591 * 4
+    assert z.q8 >= 37810 * 56 * 128 and z.q_rows % 256 == 0
+    assert z.v8 == 56 * 591 * 128 * 64 and z.k8 == 56 * 37824 * 128
+    assert z.workspace >= 2 * 56 * 591 * 128 * 4
+
+
+def test_v8_slot_order_is_a_permutation(sage):
+    keys = sage.v8_slot_keys()
+    assert sorted(keys) == list(range(64))
+    from quantized_exact_order_amd._lib import lib
+    assert lib.sage_v8_key_of_slot(64) == -1 and lib.sage_v8_key_of_slot(-1) == -1
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(N=0), "SAGE_E_SHAPE"), (dict(B=0), "SAGE_E_SHAPE"), (dict(D=64), "SAGE_E_SHAPE"),
+    (dict(N=(1 << 24) + 1), "SAGE_E_SHAPE"), (dict(Hkv=3), "SAGE_E_GQA"),
+    (dict(rope_dim=95), "SAGE_E_ROPE"), (dict(rope_dim=130), "SAGE_E_ROPE"),
+    (dict(rope_dim=-2), "SAGE_E_ROPE"), (dict(hadamard=True), "SAGE_E_UNSUPPORTED"),
+    (dict(eps=0.0), "SAGE_E_UNSUPPORTED"), (dict(eps=float("nan")), "SAGE_E_UNSUPPORTED"),
+])
+def test_shape_refusals(sage, kw, err):
+    base = dict(B=1, N=100, Hq=4, Hkv=2, D=128, rope_dim=96, hadamard=False, eps=1e-5)
+    base.update(kw)
+    with pytest.raises(sage.SageError) as ei:
+        sage.buffer_sizes(sage.Shape(**base))
+    assert ei.value.name == err
+
+
+def _call_prep(fn, shape, q=None, k=None, v=None, bufs=None, ws=0x10000, ws_bytes=1 << 40,
+               cos=0x2000, sin=0x3000, wq=None):
+    from quantized_exact_order_amd._lib import SageView, SageBufs
+    A = 0x100000
+    good = SageView(A, 0, 3 * 4 * 128, 128, 1)
+    q = q or good
+    k = k or good
+    v = v or good
+    bufs = bufs or SageBufs(A, A, A, A, A, A, A)
+    return fn(ctypes.byref(shape.c()), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), wq, None,
+              cos, sin, ctypes.byref(bufs), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["sage_prep", "sage_quant_qk"])
+def test_pass_refusals_happen_before_launch(sage, which):
+    from quantized_exact_order_amd._lib import lib, SageView, SageBufs, STATUS_NAMES
+    fn = getattr(lib, which)
+    shape = sage.Shape(1, 100, 4, 4, 128, 96)
+    A = 0x100000
+    name = lambda st: STATUS_NAMES[st]
+    assert name(_call_prep(fn, shape, q=SageView(0, 0, 512, 128, 1))) == "SAGE_E_NULL"
+    assert name(_call_prep(fn, shape, k=SageView(A, 0, 512, 128, 2))) == "SAGE_E_STRIDE"
+    assert name(_call_prep(fn, shape, v=SageView(A + 2, 0, 512, 128, 1))) == "SAGE_E_ALIGN"
+    assert name(_call_prep(fn, shape, q=SageView(A, 0, 513, 128, 1))) == "SAGE_E_ALIGN"
+    assert name(_call_prep(fn, shape, bufs=SageBufs(A, A, 0, A, A, A, A))) == "SAGE_E_NULL"
+    assert name(_call_prep(fn, shape, bufs=SageBufs(A, A, A + 4, A, A, A, A))) == "SAGE_E_ALIGN"
+    assert name(_call_prep(fn, shape, ws=0)) == "SAGE_E_WORKSPACE"
+    assert name(_call_prep(fn, shape, ws_bytes=16)) == "SAGE_E_WORKSPACE"
+    assert name(_call_prep(fn, shape, cos=None)) == "SAGE_E_NULL"
+    assert name(_call_prep(fn, shape, cos=0x2002)) == "SAGE_E_ALIGN"
+    assert name(_call_prep(fn, shape, wq=0x4008)) == "SAGE_E_ALIGN"
+    bad = sage.Shape(1, 100, 4, 4, 128, 97)
+    assert name(_call_prep(fn, bad)) == "SAGE_E_ROPE"
+
+
+def test_attn_refusals_happen_before_launch(sage):
+    from quantized_exact_order_amd._lib import lib, SageBufs, STATUS_NAMES
+    A = 0x100000
+    shape = sage.Shape(1, 100, 4, 2, 128, 96)
+    bufs = SageBufs(A, A, A, A, A, A, A)
+    call = lambda o, sb, sn, sh, b=bufs: STATUS_NAMES[lib.sage_attn_fwd(
+        ctypes.byref(shape.c()), ctypes.byref(b), o, sb, sn, sh, None)]
+    assert call(None, 0, 512, 128) == "SAGE_E_NULL"
+    assert call(A, 0, 1024, 128) == "SAGE_E_STRIDE"        # rows not contiguous in (h, d)
+    assert call(A, 0, 512, 256) == "SAGE_E_STRIDE"
+    assert call(A + 8, 0, 512, 128) == "SAGE_E_ALIGN"
+    assert call(A, 0, 512, 128, SageBufs(A, 0, A, A, A, A, A)) == "SAGE_E_NULL"

@@ -1,0 +1,116 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Preparation outputs (k_mean, v_scale, q8, q_scale, k8, k_scale, v8) must be
+byte-identical; the BF16 attention output must be within max-abs 2e-2 and
+cosine 0.999 of the oracle (overall and per head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (assert_prep_bit_exact, banner, bf16_bits, compare_output, host_tensors,
+                      run_path, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(inp, label, attn_rows=None):
+    banner(f"{label}: N={inp.q.shape[1]} Hq={inp.cfg.Hq} Hkv={inp.cfg.Hkv} D={inp.cfg.D}")
+    ref = oracle.prepare(inp)
+    shape, bufs, o = run_path(inp)
+    assert_prep_bit_exact(ref, host_tensors(shape, bufs), label)
+    B, N, Hq, D = o.shape
+    if attn_rows is None:
+        o_ref = oracle.bf16_to_f32(oracle.attention(ref))               # [B,N,Hq,D]
+        o_gpu = oracle.bf16_to_f32(bf16_bits(o))
+        compare_output(o_gpu, o_ref, label)
+        for h in range(Hq):
+            compare_output(o_gpu[:, :, h], o_ref[:, :, h], f"{label} head {h}")
+    else:
+        o_ref = oracle.bf16_to_f32(oracle.attn_rows(ref, attn_rows))
+        og = o.cpu()
+        o_gpu = np.stack([oracle.bf16_to_f32(bf16_bits(og[b, i, h])) for b, h, i in attn_rows])
+        compare_output(o_gpu, o_ref, label)
+    return ref, shape, bufs, o
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail"])
+def test_config_full(name):
+    _full_check(workloads.make_inputs(workloads.CONFIGS[name]), name)
+
+
+@pytest.mark.parametrize("layer", [0, 13, 26])
+def test_encoder_layer(layer):
+    cfg = workloads.CONFIGS["encoder"]
+    _full_check(workloads.make_inputs(cfg, layer=layer), f"encoder layer {layer}")
+
+
+def _sample_rows(B, H, N, per_head, rng, tail=64):
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            pick = set(rng.choice(N, size=min(per_head, N), replace=False).tolist())
+            pick |= set(range(min(32, N)))                       # first Q group
+            pick |= set(range(max(0, N - tail), N))              # ragged last Q tile
+            rows += [(b, h, i) for i in sorted(pick)]
+    return np.array(rows, np.int32)
+
+
+@pytest.mark.timeout(600)
+def test_gqa_hadamard_d256():
+    cfg = workloads.CONFIGS["gqa"]
+    inp = workloads.make_inputs(cfg)
+    rng = np.random.default_rng(40)
+    rows = _sample_rows(1, cfg.Hq, cfg.N, 48, rng, tail=8)
+    _full_check(inp, "gqa", attn_rows=rows)
+
+
+@pytest.mark.timeout(900)
+def test_canonical_interleaved_sampled():
+    cfg = workloads.CONFIGS["canonical"]
+    inp = workloads.make_inputs(cfg)
+    rng = np.random.default_rng(41)
+    rows = []
+    for h in (0, 27, 55):
+        pick = set(rng.choice(cfg.N, size=48, replace=False).tolist())
+        pick |= set(range(0, 32)) | set(range(cfg.N - 50, cfg.N))     # first group, 50-row tail
+        rows += [(0, h, i) for i in sorted(pick)]
+    _full_check(inp, "canonical", attn_rows=np.array(rows, np.int32))
+
+
+EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 768]
+
+
+@pytest.mark.parametrize("N", EDGE_N)
+def test_edge_lengths_d128(N):
+    inp = workloads.make_custom(1, N, 2, 2, 128, 96, seed=100 + N)
+    _full_check(inp, f"edge N={N}")
+
+
+@pytest.mark.parametrize("N", [1, 17, 65, 200])
+def test_edge_lengths_d256_gqa_hadamard(N):
+    inp = workloads.make_custom(1, N, 4, 2, 256, 192, seed=200 + N, hadamard=True)
+    _full_check(inp, f"edge d256 N={N}")
+
+
+@pytest.mark.parametrize("R", [0, 2, 40, 128])
+def test_rope_dims(R):
+    # R/2 not a multiple of 8 takes the per-element RoPE path
+    inp = workloads.make_custom(1, 150, 2, 1, 128, R, seed=300 + R)
+    _full_check(inp, f"rope_dim={R}")
+
+
+def test_extreme_outliers_and_weights():
+    inp = workloads.make_custom(1, 333, 3, 3, 128, 96, seed=400, weights=(0.5, 1.5),
+                                outlier_frac=0.02, outlier_mult=1000.0)
+    _full_check(inp, "outliers x1000")
+
+
+def test_batch_two_and_zero_rows():
+    inp = workloads.make_custom(2, 190, 2, 2, 128, 96, seed=500)
+    inp.q[1, 5] = 0            # a zero query row (all scores 0, averages V)
+    inp.k[0, 77] = 0           # a zero key row
+    inp.v[:, :, 1, 9] = 0      # an all-zero V channel: amax floored at 1e-7
+    _full_check(inp, "batch 2 with zero rows")

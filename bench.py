@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized attention forward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: sage_prep (RMSNorm + RoPE of K, K mean, V maxima), sage_quant_qk (INT8
+Q/K, E4M3 V) and sage_attn_fwd (INT8 QK, online softmax, E4M3 PV).  The
+workload is the canonical boundary of the contract page: B=1, N=37,810, 56
+heads, D=128, Q/K/V as strided views of one interleaved BF16 QKV buffer.
+
+Prints one JSON line:
+  value      4*N^2*H*D / (step time)  [TFLOPS], whole path
+  roofline   the attention kernel alone against the dense INT8/FP8 MFMA peak,
+             timed with HIP events on the stream the kernel runs on
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense INT8 / FP8 MFMA (5.0 POP/s)
+METRIC = "attention TFLOPS (4·N²·H·D/t) at N=37810,H=56,D=128; % INT8/FP8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_canonical_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "quantized_exact_order_amd", "csrc", "attn.hip")
+
+
+def _attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attn.hip", "device.h"):
+        with open(os.path.join(ROOT, "quantized_exact_order_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per attention launch from committed counter runs, or None when
+    the kernel source changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != _attn_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, cfg, budget_s: float = 12.0, heads=(0, 27, 55)):
+    """The oracle, as it stands, on a bounded sample: the full preparation, then
+    attention rows of `heads` in batches until about budget_s seconds of
+    attention work are done; the attention time is extrapolated to all N*H
+    rows."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    p = oracle.prepare(inp)
+    t_prep = time.perf_counter() - t0
+    rng = np.random.default_rng(7)
+    order = [(h, i) for h in heads for i in rng.permutation(cfg.N)]
+    rng.shuffle(order)
+    done, t_rows, batch = 0, 0.0, 256
+    while t_rows < budget_s and done < len(order):
+        rows = np.array([[0, h, i] for h, i in order[done:done + batch]], np.int32)
+        t0 = time.perf_counter()
+        oracle.attn_rows(p, rows)
+        t_rows += time.perf_counter() - t0
+        done += len(rows)
+        batch = min(batch * 2, 16384)
+    total_rows = cfg.B * cfg.Hq * cfg.N
+    t_full = t_prep + t_rows * total_rows / done
+    return {
+        "value": round(cfg.attn_ops / t_full / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"full preparation ({t_prep:.1f} s) + attention of {done} query rows of heads "
+                   f"{list(heads)} ({t_rows:.1f} s), attention time extrapolated to all "
+                   f"{total_rows} rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
+              "shards by head with no exchange, so one GPU's throughput is the measured figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import quantized_exact_order_amd as sage
+
+    cfg = workloads.CONFIGS["canonical"]
+    print(f"[bench] generating canonical inputs N={cfg.N} H={cfg.Hq} D={cfg.D}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    buf = inp.qkv.to(dev)
+    Hq, Hkv, D, B, N = cfg.Hq, cfg.Hkv, cfg.D, cfg.B, cfg.N
+    q = buf[:, :, 0:Hq * D].view(B, N, Hq, D)
+    k = buf[:, :, Hq * D:(Hq + Hkv) * D].view(B, N, Hkv, D)
+    v = buf[:, :, (Hq + Hkv) * D:].view(B, N, Hkv, D)
+    w_q, w_k = inp.w_q.to(dev), inp.w_k.to(dev)
+    cos, sin = inp.cos.to(dev).contiguous(), inp.sin.to(dev).contiguous()
+    shape = sage.Shape(B, N, Hq, Hkv, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+    bufs = sage.Buffers.allocate(shape, dev)
+    o = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        sage.prep(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+        sage.quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        sage.attn_fwd(shape, bufs, o, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    ms_step = elapsed * 1e3 / args.steps
+
+    ops = cfg.attn_ops
+    achieved = ops / (attn_avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+e4m3",
+        "data": "synthetic",
+        "config": {"workload": "canonical: B=1 N=37810 H=56 D=128, Q/K/V strided views of one "
+                               "BF16 [N,21504] QKV buffer, RMSNorm+RoPE(0-95), K smoothing, "
+                               "INT8 QK, E4M3 PV, non-causal",
+                   "B": B, "N": N, "H": Hq, "D": D, "step": "sage_prep+sage_quant_qk+sage_attn_fwd"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel<128>",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+            "traffic": _traffic(),
+            "avg_launch_ms": round(attn_avg_ms, 4),
+            "median_launch_ms": round(attn_ms[len(attn_ms) // 2], 4),
+            "ops_per_launch": ops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,11 +51,21 @@ constexpr int kBias = 0x4B400000;         // FP32 bits of 12582912 = 1.5 * 2^23
 constexpr float kBiasF = 12582912.0f;
 
 // LDS byte offset of 16-byte chunk `j` of K row `r` (row length D bytes).
+// The XOR swizzle spreads the 16 lanes that read chunk j of rows r..r+15
+// over distinct 16-byte bank groups, whether the LDS serves 8 lanes from 32
+// banks or 16 lanes from 64 banks per cycle.
 template <int D>
-__device__ __forceinline__ int k_lds(int r, int j) { return r * D + 16 * (j ^ (r & 7)); }
+__device__ __forceinline__ int k_lds(int r, int j) {
+    const int h = (D == 128) ? ((r & 7) ^ ((r >> 3) & 1)) : (r & 15);
+    return r * D + 16 * (j ^ h);
+}
 
-// LDS byte offset of 16-byte chunk `j` (0..3) of V^T row `d` (64 bytes).
-__device__ __forceinline__ int v_lds(int d, int j) { return d * 64 + 16 * (j ^ ((d >> 1) & 3)); }
+// LDS byte offset of 16-byte chunk `j` (0..3) of V^T row `d` (64 bytes),
+// swizzled the same way for rows d..d+15.
+__device__ __forceinline__ int v_lds(int d, int j) {
+    const int h = ((d >> 1) & 1) ^ (((d >> 2) & 1) << 1) ^ ((d >> 3) & 1);
+    return d * 64 + 16 * (j ^ h);
+}
 
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
 
@@ -230,26 +240,34 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fwd_kernel(const AttnParam
         SAGE_LOAD(stv, vbase, 1);
         __syncthreads();                             // every wave has read K0
 
-        for (int t = 0; t < nk - 1; ++t) {
-            const int cur = t & 1;
-            v16i sn0, sn1;
-            qk_tile<D>(kbuf[cur ^ 1], qf, col, hi, sn0, sn1);   // S(t+1) in flight
-            const float f = qc * ksc[t];
-            softmax_pv<D, false>(sc0, sc1, vbuf[cur], f, col, hi, 64, m, dsum, acc);
-            SAGE_STORE_K(cur);                       // K(t+2) over K(t)
-            SAGE_STORE_V(cur ^ 1);                   // V(t+1) over V(t-1)
-            __syncthreads();
-            SAGE_LOAD(stk, kbase, t + 3);
-            SAGE_LOAD(stv, vbase, t + 2);
+#define SAGE_PIPE_STEP(T, CUR, SC0, SC1, SN0, SN1)                                          \
+    do {                                                                                    \
+        qk_tile<D>(kbuf[(CUR) ^ 1], qf, col, hi, SN0, SN1);      /* S(T+1) in flight */     \
+        softmax_pv<D, false>(SC0, SC1, vbuf[CUR], qc * ksc[T], col, hi, 64, m, dsum, acc);  \
+        SAGE_STORE_K(CUR);                                       /* K(T+2) over K(T)   */   \
+        SAGE_STORE_V((CUR) ^ 1);                                 /* V(T+1) over V(T-1) */   \
+        __syncthreads();                                                                    \
+        SAGE_LOAD(stk, kbase, (T) + 3);                                                     \
+        SAGE_LOAD(stv, vbase, (T) + 2);                                                     \
+    } while (0)
+        v16i sn0, sn1;
+        int t = 0;
+        for (; t + 2 < nk; t += 2) {                 // tiles t, t+1 (both before the last)
+            SAGE_PIPE_STEP(t, 0, sc0, sc1, sn0, sn1);
+            SAGE_PIPE_STEP(t + 1, 1, sn0, sn1, sc0, sc1);
+        }
+        if (t < nk - 1) {
+            SAGE_PIPE_STEP(t, 0, sc0, sc1, sn0, sn1);
             sc0 = sn0;
             sc1 = sn1;
         }
-        const int t = nk - 1;
-        const float f = qc * ksc[t];
+#undef SAGE_PIPE_STEP
+        const int tl = nk - 1;
+        const float f = qc * ksc[tl];
         if (tail_valid < 64)
-            softmax_pv<D, true>(sc0, sc1, vbuf[t & 1], f, col, hi, tail_valid, m, dsum, acc);
+            softmax_pv<D, true>(sc0, sc1, vbuf[tl & 1], f, col, hi, tail_valid, m, dsum, acc);
         else
-            softmax_pv<D, false>(sc0, sc1, vbuf[t & 1], f, col, hi, 64, m, dsum, acc);
+            softmax_pv<D, false>(sc0, sc1, vbuf[tl & 1], f, col, hi, 64, m, dsum, acc);
     } else {
         // one tile of scores live at a time (wide heads): K(t), V(t) share a
         // buffer index; tile t+1 is staged while tile t is processed

@@ -33,16 +33,21 @@
 // float(S) = bits - 12582912.0f exactly (one subtraction), and the integer
 // maximum of the biased values is the maximum of S.
 //
-// Schedule (PIPE, per wave, tile t): issue the QK MFMAs of tile t+1, then the
-// softmax VALU work of tile t runs while they execute, then the PV MFMAs of
-// tile t.  K is therefore staged in LDS one tile ahead of V (two K buffers,
-// two V buffers, register-staged global loads issued a full tile ahead).
-// Wide heads (D = 256) keep one tile of scores live instead (!PIPE) to stay
-// within the register file.
+// Schedules.  Heads of D = 128 run attn_ilv_kernel: 4 waves (128 query rows)
+// per work-group, 2 work-groups per CU (2 waves per SIMD, which is what lets
+// plain VALU instructions of the two waves issue side by side).  Each wave
+// software-pipelines its tiles: iteration t holds S(t), the packed P(t-1) and
+// the LDS tiles K(t+1), V(t-1), and interleaves the QK MFMAs of tile t+1 and
+// the PV MFMAs of tile t-1 with the softmax of tile t in fenced slots.  K and
+// V tiles are copied from global memory straight into the swizzled LDS
+// layout (global_load_lds), a full iteration ahead.  Wide heads (D = 256)
+// run attn_wide_kernel, which keeps one tile of scores live to stay within
+// the register file and stages tiles through registers.
 // Work-groups are renumbered so that consecutive query tiles of a head run on
 // the same XCD and share its L2.
 
 #include "device.h"
+
 
 namespace sage {
 namespace {
@@ -173,8 +178,8 @@ __device__ __forceinline__ void stage_store_v(const v4i (&src)[CH], uint8_t *vb,
     }
 }
 
-template <int D, int WAVES, bool PIPE>
-__global__ __launch_bounds__(64 * WAVES, 1) void attn_fwd_kernel(const AttnParams p) {
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnParams p) {
     constexpr int THREADS = 64 * WAVES;
     constexpr int QTILE = 32 * WAVES;                // query rows per work-group
     constexpr int KS = D / 32;                       // QK k-steps == PV output blocks
@@ -225,78 +230,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fwd_kernel(const AttnParam
     float m = -5000000.0f;
     float dsum = hi ? 0.0f : 1.0f;                   // d0 = 1 once per row
 
-    if constexpr (PIPE) {
-        // prologue: K0, V0, K1 into LDS; S(0); then K2 / V1 in flight
-        SAGE_LOAD(stk, kbase, 0);
-        SAGE_LOAD(stv, vbase, 0);
-        SAGE_STORE_K(0);
-        SAGE_STORE_V(0);
-        SAGE_LOAD(stk, kbase, 1);
-        SAGE_STORE_K(1);
-        __syncthreads();
+    // one tile of scores live at a time (wide heads): K(t), V(t) share a
+    // buffer index; tile t+1 is staged while tile t is processed
+    SAGE_LOAD(stk, kbase, 0);
+    SAGE_LOAD(stv, vbase, 0);
+    SAGE_STORE_K(0);
+    SAGE_STORE_V(0);
+    SAGE_LOAD(stk, kbase, 1);
+    SAGE_LOAD(stv, vbase, 1);
+    __syncthreads();
+    for (int t = 0; t < nk - 1; ++t) {
+        const int cur = t & 1;
         v16i sc0, sc1;
-        qk_tile<D>(kbuf[0], qf, col, hi, sc0, sc1);
-        SAGE_LOAD(stk, kbase, 2);
-        SAGE_LOAD(stv, vbase, 1);
-        __syncthreads();                             // every wave has read K0
-
-#define SAGE_PIPE_STEP(T, CUR, SC0, SC1, SN0, SN1)                                          \
-    do {                                                                                    \
-        qk_tile<D>(kbuf[(CUR) ^ 1], qf, col, hi, SN0, SN1);      /* S(T+1) in flight */     \
-        softmax_pv<D, false>(SC0, SC1, vbuf[CUR], qc * ksc[T], col, hi, 64, m, dsum, acc);  \
-        SAGE_STORE_K(CUR);                                       /* K(T+2) over K(T)   */   \
-        SAGE_STORE_V((CUR) ^ 1);                                 /* V(T+1) over V(T-1) */   \
-        __syncthreads();                                                                    \
-        SAGE_LOAD(stk, kbase, (T) + 3);                                                     \
-        SAGE_LOAD(stv, vbase, (T) + 2);                                                     \
-    } while (0)
-        v16i sn0, sn1;
-        int t = 0;
-        for (; t + 2 < nk; t += 2) {                 // tiles t, t+1 (both before the last)
-            SAGE_PIPE_STEP(t, 0, sc0, sc1, sn0, sn1);
-            SAGE_PIPE_STEP(t + 1, 1, sn0, sn1, sc0, sc1);
-        }
-        if (t < nk - 1) {
-            SAGE_PIPE_STEP(t, 0, sc0, sc1, sn0, sn1);
-            sc0 = sn0;
-            sc1 = sn1;
-        }
-#undef SAGE_PIPE_STEP
-        const int tl = nk - 1;
-        const float f = qc * ksc[tl];
-        if (tail_valid < 64)
-            softmax_pv<D, true>(sc0, sc1, vbuf[tl & 1], f, col, hi, tail_valid, m, dsum, acc);
-        else
-            softmax_pv<D, false>(sc0, sc1, vbuf[tl & 1], f, col, hi, 64, m, dsum, acc);
-    } else {
-        // one tile of scores live at a time (wide heads): K(t), V(t) share a
-        // buffer index; tile t+1 is staged while tile t is processed
-        SAGE_LOAD(stk, kbase, 0);
-        SAGE_LOAD(stv, vbase, 0);
-        SAGE_STORE_K(0);
-        SAGE_STORE_V(0);
-        SAGE_LOAD(stk, kbase, 1);
-        SAGE_LOAD(stv, vbase, 1);
+        qk_tile<D>(kbuf[cur], qf, col, hi, sc0, sc1);
+        softmax_pv<D, false>(sc0, sc1, vbuf[cur], qc * ksc[t], col, hi, 64, m, dsum, acc);
+        SAGE_STORE_K(cur ^ 1);                   // K(t+1), V(t+1) over tile t-1
+        SAGE_STORE_V(cur ^ 1);
         __syncthreads();
-        for (int t = 0; t < nk - 1; ++t) {
-            const int cur = t & 1;
-            v16i sc0, sc1;
-            qk_tile<D>(kbuf[cur], qf, col, hi, sc0, sc1);
-            softmax_pv<D, false>(sc0, sc1, vbuf[cur], qc * ksc[t], col, hi, 64, m, dsum, acc);
-            SAGE_STORE_K(cur ^ 1);                   // K(t+1), V(t+1) over tile t-1
-            SAGE_STORE_V(cur ^ 1);
-            __syncthreads();
-            SAGE_LOAD(stk, kbase, t + 2);
-            SAGE_LOAD(stv, vbase, t + 2);
-        }
-        const int t = nk - 1;
-        v16i sc0, sc1;
-        qk_tile<D>(kbuf[t & 1], qf, col, hi, sc0, sc1);
-        if (tail_valid < 64)
-            softmax_pv<D, true>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, tail_valid, m, dsum, acc);
-        else
-            softmax_pv<D, false>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, 64, m, dsum, acc);
+        SAGE_LOAD(stk, kbase, t + 2);
+        SAGE_LOAD(stv, vbase, t + 2);
     }
+    const int t = nk - 1;
+    v16i sc0, sc1;
+    qk_tile<D>(kbuf[t & 1], qf, col, hi, sc0, sc1);
+    if (tail_valid < 64)
+        softmax_pv<D, true>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, tail_valid, m, dsum, acc);
+    else
+        softmax_pv<D, false>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, 64, m, dsum, acc);
 #undef SAGE_LOAD
 #undef SAGE_STORE_K
 #undef SAGE_STORE_V
@@ -324,18 +284,412 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_fwd_kernel(const AttnParam
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Interleaved schedule: 4 waves (128 query rows) per work-group, two
+// work-groups per CU.  Iteration t of a wave holds the finished scores S(t),
+// the packed probabilities P(t-1) and the LDS tiles K(t+1), V(t-1); it issues
+// the PV MFMAs of tile t-1 and the QK MFMAs of tile t+1 between the softmax
+// instructions of tile t, so the matrix pipe runs while the VALU computes.
+// The accumulator sees the same operations in the same order as tile-by-tile
+// processing: RO += P(t-1) V(t-1) happens before RO *= alpha(t).
+// ---------------------------------------------------------------------------
+
+// One wave-wide copy of 1 KiB from global memory straight into LDS: lane l
+// reads 16 bytes at base + off and writes them to lds + 16 l.  Issued from
+// inline assembly so that the compiler does not treat it as a store to every
+// LDS buffer (it would then wait for the copy before the next LDS read of any
+// buffer); the copy has no register results, and the kernel waits for it
+// (vmcnt) before a barrier that precedes any read of its destination.  M0 is
+// set here for every copy.
+__device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// Source offsets of the lane's 16-byte chunks of the two 1 KiB blocks
+// (i * 4 + wave, i = 0, 1) that a wave copies of every K and every V tile,
+// chosen so that the LDS bytes land in the swizzled positions of k_lds / v_lds.
+struct DmaLane {
+    uint32_t k[2], v[2];
+};
+
+__device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
+    DmaLane dl;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = (i * 4 + wave) * 64 + lane;     // LDS chunk written by this lane
+        const int r = c >> 3, pos = c & 7;            // K: row r, chunk position pos
+        const int hk = (r & 7) ^ ((r >> 3) & 1);
+        dl.k[i] = (uint32_t)(r * 128 + 16 * (pos ^ hk));
+        const int d = c >> 2, vp = c & 3;             // V^T: row d, chunk position vp
+        const int hv = ((d >> 1) & 1) ^ (((d >> 2) & 1) << 1) ^ ((d >> 3) & 1);
+        dl.v[i] = (uint32_t)(d * 64 + 16 * (vp ^ hv));
+    }
+    return dl;
+}
+
+// The copies one iteration issues: a K tile and a V tile, each into the LDS
+// buffer (address of this wave's first block) given.
+struct DmaJob {
+    const uint8_t *ksrc, *vsrc;
+    uint32_t klds, vlds;
+};
+
+// Maximum of v over lane pairs (l, l ^ 32): one v_permlane32_swap exchanges
+// the two halves of the wave.
+__device__ __forceinline__ int max_xor32(int v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+
+// Maximum of the 16 biased scores of key block c (keys 32c + 8(r/4) +
+// 4 hi + r%4 in register r) and `x`; keys >= nvalid are left out when TAIL.
+template <bool TAIL>
+__device__ __forceinline__ int block_max(const v16i &s, int c, int hi, int nvalid, int x) {
+    int v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        v[r] = s[r];
+        if (TAIL && 32 * c + 8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) v[r] = -2147483647 - 1;
+    }
+    const int a = imax3(v[0], v[1], v[2]), b = imax3(v[3], v[4], v[5]), d = imax3(v[6], v[7], v[8]);
+    const int e = imax3(v[9], v[10], v[11]), g = imax3(v[12], v[13], v[14]);
+    return imax3(imax3(a, b, d), imax3(e, g, v[15]), x);
+}
+
+// Online-softmax statistics of a tile whose lane maximum (biased) is mx:
+// m' = max(m, float(max S) * f - 8.807), alpha = 2^(m - m'), d *= alpha.
+// `moved` tells whether any row of the wave changed its maximum (alpha is
+// exactly 1 for the others).
+__device__ __forceinline__ void row_stats(int mx, float f, float &m, float &alpha, bool &moved,
+                                          float &dsum) {
+    mx = max_xor32(mx);
+    const float M = (__int_as_float(mx) - kBiasF) * f - 8.807f;
+    const float mnew = __builtin_fmaxf(m, M);
+    alpha = __builtin_amdgcn_exp2f(m - mnew);
+    moved = __any(mnew != m);
+    m = mnew;
+    dsum = dsum * alpha;
+}
+
+// One iteration t.  On entry m, alpha, moved and dsum already account for
+// the maximum of S(t) = (sc0, sc1) (scale fc), and RO holds the tiles before
+// t - 1 at the previous maximum.  The iteration
+//   - turns S(t) into probabilities (d += p, FP8 packing into pcur),
+//   - when NEXT, computes S(t+1) = K(t+1) Q^T into (sn0, sn1) from the LDS
+//     tile kt, and then its maximum (scale fn; TAILN masks keys >= nvalid)
+//     into m, alpha, moved, dsum for the next iteration,
+//   - when PREV, adds P(t-1) V(t-1) (pprev, LDS tile vt) to RO, and then
+//     rescales RO by alpha(t),
+// which is the per-tile order RO = RO alpha(t) + P(t) V(t) with the PV of
+// each tile deferred by one iteration.  TAILC masks keys >= nvalid of S(t).
+//
+// The instructions are laid out in 13 slots separated by scheduling fences:
+// slots 1-8 each issue one QK MFMA beside one group of four exponentials
+// with their FP8 packing, slots 9-12 each issue one PV MFMA beside the row
+// maximum of S(t+1); the LDS fragment reads run one or two slots ahead of
+// their MFMA and the four tile copies of the iteration (job) go out one per
+// slot, so that the copies of all waves do not queue up at once.
+template <bool PREV, bool NEXT, bool TAILC, bool TAILN>
+__device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i &sn0, v16i &sn1,
+                                         const v8i &pprev, v8i &pcur, const uint8_t *kt,
+                                         const uint8_t *vt, const v4i (&qf)[4], float fc, float fn,
+                                         int col, int hi, int nvalid, float &m, float &alpha,
+                                         bool &moved, float &dsum, v16f (&acc)[4], const DmaJob &job,
+                                         const DmaLane &dl) {
+    constexpr int D = 128;
+#define SAGE_FENCE __builtin_amdgcn_sched_barrier(0)
+    int a[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { a[r] = sc0[r]; a[16 + r] = sc1[r]; }
+    v8i vf[4];
+    v4i kf[8];
+    auto rd_v = [&](int blk) {
+        if constexpr (PREV) {
+            const int d = 32 * blk + col;
+            const v4i x0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+            const v4i x1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+            vf[blk] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+    };
+    auto mf_v = [&](int blk) {
+        if constexpr (PREV)
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[blk], pprev, acc[blk], 0, 0, 0, 0, 0, 0);
+    };
+    // QK MFMA j: k-step j >> 1 of key block j & 1 (the two accumulation
+    // chains alternate)
+    auto rd_k = [&](int j) {
+        if constexpr (NEXT)
+            kf[j] = *reinterpret_cast<const v4i *>(kt + k_lds<D>(32 * (j & 1) + col, 2 * (j >> 1) + hi));
+    };
+    auto mf_k = [&](int j) {
+        if constexpr (NEXT) {
+            v16i &sn = (j & 1) ? sn1 : sn0;
+            const v16i c = (j < 2) ? v16i{kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                                          kBias, kBias, kBias, kBias, kBias, kBias, kBias}
+                                   : sn;
+            sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[j], qf[j >> 1], c, 0, 0, 0);
+        }
+    };
+    const float nm = -m;
+    int pk[8];
+    auto grp = [&](int q) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = 4 * q + i;
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(a[idx]) - kBiasF, fc, nm));
+            if (TAILC && 32 * (idx >> 4) + 8 * ((idx & 15) >> 2) + 4 * hi + (idx & 3) >= nvalid) e = 0.0f;
+            pr[i] = e;
+            dsum = dsum + e;
+        }
+        // bytes 2-3 of the first pack are overwritten by the second: the
+        // first operand's own register (dead afterwards) serves as the old value
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __float_as_int(pr[0]), false);
+        pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+        // keep the group in its slot (IR passes would otherwise sink it to
+        // the first use, past the rescale branch)
+        asm volatile("" ::"v"(pk[q]), "v"(dsum));
+    };
+
+    rd_k(0); rd_k(1); grp(0); SAGE_FENCE;
+    mf_k(0); lds_dma16(job.ksrc, dl.k[0], job.klds); rd_k(2); grp(1); SAGE_FENCE;
+    mf_k(1); lds_dma16(job.ksrc, dl.k[1], job.klds + 4096); rd_k(3); grp(2); SAGE_FENCE;
+    mf_k(2); lds_dma16(job.vsrc, dl.v[0], job.vlds); rd_k(4); grp(3); SAGE_FENCE;
+    mf_k(3); lds_dma16(job.vsrc, dl.v[1], job.vlds + 4096); rd_k(5); grp(4); SAGE_FENCE;
+    mf_k(4); rd_k(6); grp(5); SAGE_FENCE;
+    mf_k(5); rd_k(7); rd_v(0); grp(6); SAGE_FENCE;
+    mf_k(6); rd_v(1); grp(7); SAGE_FENCE;
+    mf_k(7); rd_v(2); SAGE_FENCE;
+    const float alpha_c = alpha;
+    const bool moved_c = moved;
+    int x0 = 0;
+    mf_v(0); rd_v(3);
+    if constexpr (NEXT) x0 = block_max<TAILN>(sn0, 0, hi, nvalid, -2147483647 - 1);
+    SAGE_FENCE;
+    mf_v(1);
+    if constexpr (NEXT) x0 = block_max<TAILN>(sn1, 1, hi, nvalid, x0);
+    SAGE_FENCE;
+    mf_v(2);
+    if constexpr (NEXT) {
+        row_stats(x0, fn, m, alpha, moved, dsum);
+        asm volatile("" ::"v"(m), "v"(alpha), "v"(dsum), "s"((int)moved));
+    }
+    SAGE_FENCE;
+    mf_v(3); SAGE_FENCE;
+#undef SAGE_FENCE
+    pcur = v8i{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+    if (PREV && moved_c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] * alpha_c;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
+    constexpr int THREADS = 256, QTILE = 128;
+    constexpr int KS = D / 32;
+    constexpr int KT = 64 * D;
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][KT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, col = lane & 31;
+
+    const int total = gridDim.x, nxcd = 8;
+    const int xq = total / nxcd, xr = total % nxcd;
+    const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
+    const int lid = x * xq + min(x, xr) + k;
+    const int nqt = (p.N + QTILE - 1) / QTILE;
+    const int qt = lid % nqt, h = (lid / nqt) % p.Hq, b = lid / (nqt * p.Hq);
+    const int hk = h / p.grp;
+    const int q0 = qt * QTILE + 32 * wave;
+    const int g = q0 >> 5;
+
+    const int8_t *qrow = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + q0 + col) * D + 16 * hi;
+    v4i qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const v4i *>(qrow + 32 * s);
+    const float qs = (g < p.nq) ? p.q_scale[((int64_t)b * p.Hq + h) * p.nq + g] : 1.0f;
+    const float qc = qs * p.c;
+
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
+    const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
+    const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
+    const int nk = p.nk;
+    const int tail_valid = p.N - 64 * (nk - 1);
+    const bool tail = tail_valid < 64;
+
+    v16f acc[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) acc[i] = v16f{};
+    float m = -5000000.0f, alpha = 1.0f;
+    bool moved = false;
+    float dsum = hi ? 0.0f : 1.0f;
+    // k_scale of tiles t and t+1 while iteration t runs; the one of tile t+2
+    // is loaded at its start (ahead of the tile copies, so that waiting for
+    // it never waits for them) and used an iteration later
+    float ks0 = ksc[0], ks1 = ksc[min(1, nk - 1)], ks2;
+
+    const DmaLane dl = dma_lane(wave, lane);
+    const uint32_t kl0 = lds_addr(kbuf[0]) + 1024 * wave, kl1 = lds_addr(kbuf[1]) + 1024 * wave;
+    const uint32_t vl0 = lds_addr(vbuf[0]) + 1024 * wave, vl1 = lds_addr(vbuf[1]) + 1024 * wave;
+
+    // prologue: K(0), K(1) resident, S(0) and its maximum
+    lds_dma16(kbase, dl.k[0], kl0);
+    lds_dma16(kbase, dl.k[1], kl0 + 4096);
+    if (nk > 1) {
+        lds_dma16(kbase + KT, dl.k[0], kl1);
+        lds_dma16(kbase + KT, dl.k[1], kl1 + 4096);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    v16i sa0, sa1, sb0, sb1;
+    v8i pa, pb;
+    qk_tile<D>(kbuf[0], qf, col, hi, sa0, sa1);
+    {
+        int mx;
+        if (nk == 1 && tail)
+            mx = block_max<true>(sa1, 1, hi, tail_valid, block_max<true>(sa0, 0, hi, tail_valid, -2147483647 - 1));
+        else
+            mx = block_max<false>(sa1, 1, hi, 64, block_max<false>(sa0, 0, hi, 64, -2147483647 - 1));
+        row_stats(mx, qc * ks0, m, alpha, moved, dsum);
+    }
+
+    // iteration t: wait for K(t+1) / V(t-1), barrier (K(t), V(t-2) consumed);
+    // the iteration then copies K(t+2) and V(t) into the buffers those
+    // occupied (K(nk-1) again, unread, once t + 2 runs past the last tile)
+    DmaJob job;
+#define SAGE_ILV_SYNC(T)                                                                       \
+    do {                                                                                       \
+        __builtin_amdgcn_s_waitcnt(0x0F70);                                                    \
+        __syncthreads();                                                                       \
+        ks2 = ksc[min((T) + 2, nk - 1)];                                                       \
+        job.ksrc = kbase + (int64_t)min((T) + 2, nk - 1) * KT;                                 \
+        job.vsrc = vbase + (int64_t)(T) * KT;                                                  \
+        job.klds = ((T) & 1) ? kl1 : kl0;                                                      \
+        job.vlds = ((T) & 1) ? vl1 : vl0;                                                      \
+    } while (0)
+#define SAGE_ILV_ARGS(T) qf, qc * ks0, qc * ks1, col, hi, tail_valid, m, alpha, moved, dsum, acc, job, dl
+
+    int t = 0;
+    if (nk > 1) {
+        SAGE_ILV_SYNC(0);
+        if (nk == 2 && tail)
+            ilv_step<false, true, false, true>(sa0, sa1, sb0, sb1, pb, pa, kbuf[1], nullptr, SAGE_ILV_ARGS(0));
+        else
+            ilv_step<false, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[1], nullptr, SAGE_ILV_ARGS(0));
+        ks0 = ks1; ks1 = ks2;
+        t = 1;
+        // pairs of iterations (odd t, even t + 1) whose next tile is not the last
+        for (; t + 4 <= nk; t += 2) {
+            SAGE_ILV_SYNC(t);
+            ilv_step<true, true, false, false>(sb0, sb1, sa0, sa1, pa, pb, kbuf[(t + 1) & 1], vbuf[(t - 1) & 1],
+                                               SAGE_ILV_ARGS(t));
+            ks0 = ks1; ks1 = ks2;
+            SAGE_ILV_SYNC(t + 1);
+            ilv_step<true, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[t & 1], vbuf[t & 1],
+                                               SAGE_ILV_ARGS(t + 1));
+            ks0 = ks1; ks1 = ks2;
+        }
+        if (t + 3 <= nk) {                           // one more odd iteration of that kind
+            SAGE_ILV_SYNC(t);
+            ilv_step<true, true, false, false>(sb0, sb1, sa0, sa1, pa, pb, kbuf[(t + 1) & 1], vbuf[(t - 1) & 1],
+                                               SAGE_ILV_ARGS(t));
+            ks0 = ks1; ks1 = ks2;
+            ++t;
+        }
+        // S(t) to sa, P(t-1) to pb
+        if (t & 1) {
+            sa0 = sb0;
+            sa1 = sb1;
+            pb = pa;
+        }
+        if (t == nk - 2) {                           // the iteration whose next tile is the last
+            SAGE_ILV_SYNC(t);
+            if (tail)
+                ilv_step<true, true, false, true>(sa0, sa1, sb0, sb1, pb, pa, kbuf[(t + 1) & 1],
+                                                  vbuf[(t - 1) & 1], SAGE_ILV_ARGS(t));
+            else
+                ilv_step<true, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[(t + 1) & 1],
+                                                   vbuf[(t - 1) & 1], SAGE_ILV_ARGS(t));
+            ks0 = ks1; ks1 = ks2;
+            ++t;
+            sa0 = sb0;
+            sa1 = sb1;
+            pb = pa;
+        }
+    }
+    // the last tile t = nk - 1: S(t) in sa, P(t-1) in pb; P(t) into pa
+    SAGE_ILV_SYNC(t);
+    if (t == 0) {
+        if (tail)
+            ilv_step<false, false, true, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, nullptr, SAGE_ILV_ARGS(t));
+        else
+            ilv_step<false, false, false, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, nullptr, SAGE_ILV_ARGS(t));
+    } else {
+        if (tail)
+            ilv_step<true, false, true, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, vbuf[(t - 1) & 1],
+                                               SAGE_ILV_ARGS(t));
+        else
+            ilv_step<true, false, false, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, vbuf[(t - 1) & 1],
+                                                SAGE_ILV_ARGS(t));
+    }
+#undef SAGE_ILV_SYNC
+#undef SAGE_ILV_ARGS
+    // PV of the last tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    {
+        const uint8_t *vt = vbuf[t & 1];
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk) {
+            const int d = 32 * blk + col;
+            const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+            const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+            const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pa, acc[blk], 0, 0, 0, 0, 0, 0);
+        }
+    }
+
+    const float dt = dsum + shfl_xor_f(dsum, 32);
+    const float rinv = 1.0f / dt;
+    const int n = q0 + col;
+    if (n < p.N) {
+        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
+        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * blk + 8 * r4 + 4 * hi;
+                const float4 sc = *reinterpret_cast<const float4 *>(vs + d0);
+                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc.x;
+                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc.y;
+                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc.z;
+                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc.w;
+                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            }
+        }
+    }
+}
+
 }  // namespace
 }  // namespace sage
 
 hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s) {
     if (D == 128) {
-        constexpr int W = 8;
-        const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
-        sage::attn_fwd_kernel<128, W, true><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
+        const unsigned nqt = (unsigned)((p.N + 127) / 128);
+        sage::attn_ilv_kernel<128><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
         constexpr int W = 4;
         const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
-        sage::attn_fwd_kernel<256, W, false><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
+        sage::attn_wide_kernel<256, W><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
     }
     return hipGetLastError();
 }

@@ -311,26 +311,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)p;
 }
 
-// Source offsets of the lane's 16-byte chunks of the two 1 KiB blocks
-// (i * 4 + wave, i = 0, 1) that a wave copies of every K and every V tile,
-// chosen so that the LDS bytes land in the swizzled positions of k_lds / v_lds.
+// Source offsets of the lane's 16-byte chunks of the first 1 KiB block
+// (block `wave`) that a wave copies of every K and every V tile, chosen so
+// that the LDS bytes land in the swizzled positions of k_lds / v_lds.  Its
+// second block (wave + 4) is 32 K rows / 64 V^T rows further on, where both
+// swizzles repeat: the same offsets from a base 4096 bytes higher.
 struct DmaLane {
-    uint32_t k[2], v[2];
+    uint32_t k, v;
 };
 
 __device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
-    DmaLane dl;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = (i * 4 + wave) * 64 + lane;     // LDS chunk written by this lane
-        const int r = c >> 3, pos = c & 7;            // K: row r, chunk position pos
-        const int hk = (r & 7) ^ ((r >> 3) & 1);
-        dl.k[i] = (uint32_t)(r * 128 + 16 * (pos ^ hk));
-        const int d = c >> 2, vp = c & 3;             // V^T: row d, chunk position vp
-        const int hv = ((d >> 1) & 1) ^ (((d >> 2) & 1) << 1) ^ ((d >> 3) & 1);
-        dl.v[i] = (uint32_t)(d * 64 + 16 * (vp ^ hv));
-    }
-    return dl;
+    const int c = wave * 64 + lane;                   // LDS chunk written by this lane
+    const int r = c >> 3, pos = c & 7;                // K: row r, chunk position pos
+    const int hk = (r & 7) ^ ((r >> 3) & 1);
+    const int d = c >> 2, vp = c & 3;                 // V^T: row d, chunk position vp
+    const int hv = ((d >> 1) & 1) ^ (((d >> 2) & 1) << 1) ^ ((d >> 3) & 1);
+    return DmaLane{(uint32_t)(r * 128 + 16 * (pos ^ hk)), (uint32_t)(d * 64 + 16 * (vp ^ hv))};
 }
 
 // The copies one iteration issues: a K tile and a V tile, each into the LDS
@@ -347,16 +343,8 @@ __device__ __forceinline__ int max_xor32(int v) {
     return max((int)r[0], (int)r[1]);
 }
 
-// Maximum of the 16 biased scores of key block c (keys 32c + 8(r/4) +
-// 4 hi + r%4 in register r) and `x`; keys >= nvalid are left out when TAIL.
-template <bool TAIL>
-__device__ __forceinline__ int block_max(const v16i &s, int c, int hi, int nvalid, int x) {
-    int v[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        v[r] = s[r];
-        if (TAIL && 32 * c + 8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) v[r] = -2147483647 - 1;
-    }
+// Maximum of the 16 biased scores of a key block and `x`.
+__device__ __forceinline__ int block_max(const v16i &v, int x) {
     const int a = imax3(v[0], v[1], v[2]), b = imax3(v[3], v[4], v[5]), d = imax3(v[6], v[7], v[8]);
     const int e = imax3(v[9], v[10], v[11]), g = imax3(v[12], v[13], v[14]);
     return imax3(imax3(a, b, d), imax3(e, g, v[15]), x);
@@ -382,24 +370,26 @@ __device__ __forceinline__ void row_stats(int mx, float f, float &m, float &alph
 // t - 1 at the previous maximum.  The iteration
 //   - turns S(t) into probabilities (d += p, FP8 packing into pcur),
 //   - when NEXT, computes S(t+1) = K(t+1) Q^T into (sn0, sn1) from the LDS
-//     tile kt, and then its maximum (scale fn; TAILN masks keys >= nvalid)
-//     into m, alpha, moved, dsum for the next iteration,
+//     tile kt, and then its maximum (scale fn) into m, alpha, moved, dsum
+//     for the next iteration,
 //   - when PREV, adds P(t-1) V(t-1) (pprev, LDS tile vt) to RO, and then
 //     rescales RO by alpha(t),
 // which is the per-tile order RO = RO alpha(t) + P(t) V(t) with the PV of
-// each tile deferred by one iteration.  TAILC masks keys >= nvalid of S(t).
+// each tile deferred by one iteration.  Every key of these tiles is valid
+// (the last tile, which may be partial, takes the one-tile path).
 //
 // The instructions are laid out in 13 slots separated by scheduling fences:
-// slots 1-8 each issue one QK MFMA beside one group of four exponentials
-// with their FP8 packing, slots 9-12 each issue one PV MFMA beside the row
-// maximum of S(t+1); the LDS fragment reads run one or two slots ahead of
-// their MFMA and the four tile copies of the iteration (job) go out one per
-// slot, so that the copies of all waves do not queue up at once.
-template <bool PREV, bool NEXT, bool TAILC, bool TAILN>
+// slots 0-7 each compute one group of four exponentials with their FP8
+// packing, slots 1-8 also issue one QK MFMA each, slots 9-12 each issue one
+// PV MFMA beside the row maximum of S(t+1); the LDS fragment reads run one or
+// two slots ahead of their MFMA and the four tile copies of the iteration
+// (job) go out one per slot, so that the copies of all waves do not queue up
+// at once.
+template <bool PREV, bool NEXT>
 __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i &sn0, v16i &sn1,
                                          const v8i &pprev, v8i &pcur, const uint8_t *kt,
                                          const uint8_t *vt, const v4i (&qf)[4], float fc, float fn,
-                                         int col, int hi, int nvalid, float &m, float &alpha,
+                                         int col, int hi, float &m, float &alpha,
                                          bool &moved, float &dsum, v16f (&acc)[4], const DmaJob &job,
                                          const DmaLane &dl) {
     constexpr int D = 128;
@@ -444,7 +434,6 @@ __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i 
         for (int i = 0; i < 4; ++i) {
             const int idx = 4 * q + i;
             float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(a[idx]) - kBiasF, fc, nm));
-            if (TAILC && 32 * (idx >> 4) + 8 * ((idx & 15) >> 2) + 4 * hi + (idx & 3) >= nvalid) e = 0.0f;
             pr[i] = e;
             dsum = dsum + e;
         }
@@ -458,10 +447,10 @@ __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i 
     };
 
     rd_k(0); rd_k(1); grp(0); SAGE_FENCE;
-    mf_k(0); lds_dma16(job.ksrc, dl.k[0], job.klds); rd_k(2); grp(1); SAGE_FENCE;
-    mf_k(1); lds_dma16(job.ksrc, dl.k[1], job.klds + 4096); rd_k(3); grp(2); SAGE_FENCE;
-    mf_k(2); lds_dma16(job.vsrc, dl.v[0], job.vlds); rd_k(4); grp(3); SAGE_FENCE;
-    mf_k(3); lds_dma16(job.vsrc, dl.v[1], job.vlds + 4096); rd_k(5); grp(4); SAGE_FENCE;
+    mf_k(0); lds_dma16(job.ksrc, dl.k, job.klds); rd_k(2); grp(1); SAGE_FENCE;
+    mf_k(1); lds_dma16(job.ksrc + 4096, dl.k, job.klds + 4096); rd_k(3); grp(2); SAGE_FENCE;
+    mf_k(2); lds_dma16(job.vsrc, dl.v, job.vlds); rd_k(4); grp(3); SAGE_FENCE;
+    mf_k(3); lds_dma16(job.vsrc + 4096, dl.v, job.vlds + 4096); rd_k(5); grp(4); SAGE_FENCE;
     mf_k(4); rd_k(6); grp(5); SAGE_FENCE;
     mf_k(5); rd_k(7); rd_v(0); grp(6); SAGE_FENCE;
     mf_k(6); rd_v(1); grp(7); SAGE_FENCE;
@@ -470,10 +459,10 @@ __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i 
     const bool moved_c = moved;
     int x0 = 0;
     mf_v(0); rd_v(3);
-    if constexpr (NEXT) x0 = block_max<TAILN>(sn0, 0, hi, nvalid, -2147483647 - 1);
+    if constexpr (NEXT) x0 = block_max(sn0, -2147483647 - 1);
     SAGE_FENCE;
     mf_v(1);
-    if constexpr (NEXT) x0 = block_max<TAILN>(sn1, 1, hi, nvalid, x0);
+    if constexpr (NEXT) x0 = block_max(sn1, x0);
     SAGE_FENCE;
     mf_v(2);
     if constexpr (NEXT) {
@@ -492,7 +481,7 @@ __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i 
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
-    constexpr int THREADS = 256, QTILE = 128;
+    constexpr int QTILE = 128;
     constexpr int KS = D / 32;
     constexpr int KT = 64 * D;
     __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][KT];
@@ -522,8 +511,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
     const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
     const int nk = p.nk;
-    const int tail_valid = p.N - 64 * (nk - 1);
-    const bool tail = tail_valid < 64;
+    const int tail_valid = p.N - 64 * (nk - 1);     // valid keys of the last tile (1..64)
 
     v16f acc[KS];
 #pragma unroll
@@ -540,31 +528,27 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     const uint32_t kl0 = lds_addr(kbuf[0]) + 1024 * wave, kl1 = lds_addr(kbuf[1]) + 1024 * wave;
     const uint32_t vl0 = lds_addr(vbuf[0]) + 1024 * wave, vl1 = lds_addr(vbuf[1]) + 1024 * wave;
 
-    // prologue: K(0), K(1) resident, S(0) and its maximum
-    lds_dma16(kbase, dl.k[0], kl0);
-    lds_dma16(kbase, dl.k[1], kl0 + 4096);
-    if (nk > 1) {
-        lds_dma16(kbase + KT, dl.k[0], kl1);
-        lds_dma16(kbase + KT, dl.k[1], kl1 + 4096);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    // Tiles 0 .. nk-2 run software-pipelined (all their keys are valid);
+    // the last tile, which may be partial, runs the one-tile path after the
+    // pipeline drains.  A single tile goes straight to that path.
     v16i sa0, sa1, sb0, sb1;
-    v8i pa, pb;
-    qk_tile<D>(kbuf[0], qf, col, hi, sa0, sa1);
-    {
-        int mx;
-        if (nk == 1 && tail)
-            mx = block_max<true>(sa1, 1, hi, tail_valid, block_max<true>(sa0, 0, hi, tail_valid, -2147483647 - 1));
-        else
-            mx = block_max<false>(sa1, 1, hi, 64, block_max<false>(sa0, 0, hi, 64, -2147483647 - 1));
-        row_stats(mx, qc * ks0, m, alpha, moved, dsum);
-    }
-
-    // iteration t: wait for K(t+1) / V(t-1), barrier (K(t), V(t-2) consumed);
-    // the iteration then copies K(t+2) and V(t) into the buffers those
-    // occupied (K(nk-1) again, unread, once t + 2 runs past the last tile)
+    v8i pa = {}, pb = {};
     DmaJob job;
+    if (nk > 1) {
+        // prologue: K(0), K(1) resident, S(0) and its maximum
+        lds_dma16(kbase, dl.k, kl0);
+        lds_dma16(kbase + 4096, dl.k, kl0 + 4096);
+        lds_dma16(kbase + KT, dl.k, kl1);
+        lds_dma16(kbase + KT + 4096, dl.k, kl1 + 4096);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        qk_tile<D>(kbuf[0], qf, col, hi, sa0, sa1);
+        row_stats(block_max(sa1, block_max(sa0, -2147483647 - 1)), qc * ks0, m, alpha, moved, dsum);
+
+        // iteration t: wait for K(t+1) / V(t-1), barrier (K(t), V(t-2)
+        // consumed); the iteration then copies K(t+2) and V(t) into the
+        // buffers those occupied (K(nk-1) again, unread, once t + 2 runs
+        // past the last tile)
 #define SAGE_ILV_SYNC(T)                                                                       \
     do {                                                                                       \
         __builtin_amdgcn_s_waitcnt(0x0F70);                                                    \
@@ -575,86 +559,79 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
         job.klds = ((T) & 1) ? kl1 : kl0;                                                      \
         job.vlds = ((T) & 1) ? vl1 : vl0;                                                      \
     } while (0)
-#define SAGE_ILV_ARGS(T) qf, qc * ks0, qc * ks1, col, hi, tail_valid, m, alpha, moved, dsum, acc, job, dl
-
-    int t = 0;
-    if (nk > 1) {
+#define SAGE_ILV_ARGS qf, qc * ks0, qc * ks1, col, hi, m, alpha, moved, dsum, acc, job, dl
+        // iteration t reads S(t) and P(t-1) and writes S(t+1) and P(t) in the
+        // register sets of its parity: even t (sa -> sb, pb -> pa), odd t
+        // (sb -> sa, pa -> pb), so no set is ever copied
+#define SAGE_STEP_EVEN(P, N, T)                                                                \
+    ilv_step<P, N>(sa0, sa1, sb0, sb1, pb, pa, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
+#define SAGE_STEP_ODD(P, N, T)                                                                 \
+    ilv_step<P, N>(sb0, sb1, sa0, sa1, pa, pb, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
+#define SAGE_NEXT_SCALE do { ks0 = ks1; ks1 = ks2; } while (0)
+        const int tp = nk - 2;                       // the last pipelined iteration
         SAGE_ILV_SYNC(0);
-        if (nk == 2 && tail)
-            ilv_step<false, true, false, true>(sa0, sa1, sb0, sb1, pb, pa, kbuf[1], nullptr, SAGE_ILV_ARGS(0));
-        else
-            ilv_step<false, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[1], nullptr, SAGE_ILV_ARGS(0));
-        ks0 = ks1; ks1 = ks2;
-        t = 1;
-        // pairs of iterations (odd t, even t + 1) whose next tile is not the last
-        for (; t + 4 <= nk; t += 2) {
+        if (tp == 0) SAGE_STEP_EVEN(false, false, 0);
+        else SAGE_STEP_EVEN(false, true, 0);
+        SAGE_NEXT_SCALE;
+        int t = 1;
+        for (; t + 1 < tp; t += 2) {                 // pairs (odd t, even t + 1) before tp
             SAGE_ILV_SYNC(t);
-            ilv_step<true, true, false, false>(sb0, sb1, sa0, sa1, pa, pb, kbuf[(t + 1) & 1], vbuf[(t - 1) & 1],
-                                               SAGE_ILV_ARGS(t));
-            ks0 = ks1; ks1 = ks2;
+            SAGE_STEP_ODD(true, true, t);
+            SAGE_NEXT_SCALE;
             SAGE_ILV_SYNC(t + 1);
-            ilv_step<true, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[t & 1], vbuf[t & 1],
-                                               SAGE_ILV_ARGS(t + 1));
-            ks0 = ks1; ks1 = ks2;
+            SAGE_STEP_EVEN(true, true, t + 1);
+            SAGE_NEXT_SCALE;
         }
-        if (t + 3 <= nk) {                           // one more odd iteration of that kind
+        if (t < tp) {                                // one odd iteration before tp
             SAGE_ILV_SYNC(t);
-            ilv_step<true, true, false, false>(sb0, sb1, sa0, sa1, pa, pb, kbuf[(t + 1) & 1], vbuf[(t - 1) & 1],
-                                               SAGE_ILV_ARGS(t));
-            ks0 = ks1; ks1 = ks2;
+            SAGE_STEP_ODD(true, true, t);
+            SAGE_NEXT_SCALE;
             ++t;
         }
-        // S(t) to sa, P(t-1) to pb
-        if (t & 1) {
-            sa0 = sb0;
-            sa1 = sb1;
-            pb = pa;
+        if (tp > 0) {                                // iteration tp: no next tile to score
+            SAGE_ILV_SYNC(tp);
+            if (tp & 1) SAGE_STEP_ODD(true, false, tp);
+            else SAGE_STEP_EVEN(true, false, tp);
+            SAGE_NEXT_SCALE;
         }
-        if (t == nk - 2) {                           // the iteration whose next tile is the last
-            SAGE_ILV_SYNC(t);
-            if (tail)
-                ilv_step<true, true, false, true>(sa0, sa1, sb0, sb1, pb, pa, kbuf[(t + 1) & 1],
-                                                  vbuf[(t - 1) & 1], SAGE_ILV_ARGS(t));
-            else
-                ilv_step<true, true, false, false>(sa0, sa1, sb0, sb1, pb, pa, kbuf[(t + 1) & 1],
-                                                   vbuf[(t - 1) & 1], SAGE_ILV_ARGS(t));
-            ks0 = ks1; ks1 = ks2;
-            ++t;
-            sa0 = sb0;
-            sa1 = sb1;
-            pb = pa;
-        }
-    }
-    // the last tile t = nk - 1: S(t) in sa, P(t-1) in pb; P(t) into pa
-    SAGE_ILV_SYNC(t);
-    if (t == 0) {
-        if (tail)
-            ilv_step<false, false, true, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, nullptr, SAGE_ILV_ARGS(t));
-        else
-            ilv_step<false, false, false, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, nullptr, SAGE_ILV_ARGS(t));
-    } else {
-        if (tail)
-            ilv_step<true, false, true, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, vbuf[(t - 1) & 1],
-                                               SAGE_ILV_ARGS(t));
-        else
-            ilv_step<true, false, false, false>(sa0, sa1, sb0, sb1, pb, pa, nullptr, vbuf[(t - 1) & 1],
-                                                SAGE_ILV_ARGS(t));
-    }
 #undef SAGE_ILV_SYNC
 #undef SAGE_ILV_ARGS
-    // PV of the last tile
+#undef SAGE_STEP_EVEN
+#undef SAGE_STEP_ODD
+#undef SAGE_NEXT_SCALE
+        // drain: PV of tile tp (V(tp) was copied in iteration tp; P(tp) is in
+        // pa for an even tp, pb for an odd one), and the copy of V(nk-1) into
+        // the buffer of V(tp-1)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        lds_dma16(vbase + (int64_t)(nk - 1) * KT, dl.v, (nk - 1) & 1 ? vl1 : vl0);
+        lds_dma16(vbase + (int64_t)(nk - 1) * KT + 4096, dl.v, ((nk - 1) & 1 ? vl1 : vl0) + 4096);
+        {
+            const uint8_t *vt = vbuf[tp & 1];
+            const v8i pl = (tp & 1) ? pb : pa;
+#pragma unroll
+            for (int blk = 0; blk < KS; ++blk) {
+                const int d = 32 * blk + col;
+                const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+                const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+                const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+                acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pl, acc[blk], 0, 0, 0, 0, 0, 0);
+            }
+        }
+    } else {
+        lds_dma16(kbase, dl.k, kl0);
+        lds_dma16(kbase + 4096, dl.k, kl0 + 4096);
+        lds_dma16(vbase, dl.v, vl0);
+        lds_dma16(vbase + 4096, dl.v, vl0 + 4096);
+    }
+    // the last tile (K(nk-1) was copied two iterations ahead, V(nk-1) above)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     {
-        const uint8_t *vt = vbuf[t & 1];
-#pragma unroll
-        for (int blk = 0; blk < KS; ++blk) {
-            const int d = 32 * blk + col;
-            const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
-            const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
-            const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
-            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pa, acc[blk], 0, 0, 0, 0, 0, 0);
-        }
+        const int tl = nk - 1;
+        v16i s0, s1;
+        qk_tile<D>(kbuf[tl & 1], qf, col, hi, s0, s1);
+        softmax_pv<D, true>(s0, s1, vbuf[tl & 1], qc * ksc[tl], col, hi, tail_valid, m, dsum, acc);
     }
 
     const float dt = dsum + shfl_xor_f(dsum, 32);

@@ -57,7 +57,9 @@ typedef enum sage_status {
 
 /* Problem shape.
  *   B, N      batch and sequence length (1 <= N <= 2^24)
- *   Hq, Hkv   query and key/value heads; query head h reads KV head h/(Hq/Hkv)
+ *   Hq, Hkv   query and key/value heads; query head h reads KV head h/(Hq/Hkv);
+ *             B * Hq * ceil(N/64) must stay below 2^31 (work-groups of one
+ *             launch), else SAGE_E_SHAPE
  *   D         head dimension, 128 or 256
  *   rope_dim  R: split-half RoPE rotates dims [0, R) in pairs (i, i + R/2);
  *             even, 0 <= R <= D (96 for D = 128 on the contract page)

@@ -21,6 +21,8 @@ sage_status check_shape(const sage_shape *s) {
     if (s->B < 1 || s->N < 1 || s->N > kMaxN || s->Hq < 1 || s->Hkv < 1) return SAGE_E_SHAPE;
     if (s->D != 128 && s->D != 256) return SAGE_E_SHAPE;
     if ((int64_t)s->B * s->Hq > 65535 * 64 || s->B > 65535 || s->Hq > 65535) return SAGE_E_SHAPE;
+    // every launch covers at most B * Hq * ceil(N/64) work-groups in one dimension
+    if ((int64_t)s->B * s->Hq * ((s->N + 63) / 64) > 2147483647) return SAGE_E_SHAPE;
     if (s->Hq % s->Hkv != 0) return SAGE_E_GQA;
     if (s->rope_dim < 0 || s->rope_dim > s->D || (s->rope_dim & 1)) return SAGE_E_ROPE;
     if (s->hadamard != 0 && s->hadamard != 1) return SAGE_E_UNSUPPORTED;

@@ -167,7 +167,8 @@ __device__ __forceinline__ void wht8(float u[8], int j) {
 
 // ---------------------------------------------------------------------------
 // Pass 1: K rows -> per-tile column sums (pairwise over 64 rows); V rows ->
-// per-tile column maxima of |v|.  Grid (nk, Hkv, B), 256 threads.
+// per-tile column maxima of |v|.  Grid (nk * Hkv, B), x = tile * Hkv + head,
+// 256 threads.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p) {
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
     float *vpart = reinterpret_cast<float *>(ybuf);
     static_assert(RPP * D * sizeof(float) <= sizeof(ybuf), "vpart must fit in ybuf");
 
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
 #pragma unroll
@@ -240,36 +241,87 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 
 // ---------------------------------------------------------------------------
 // Pass 1b: per (b, h, d) the pairwise tree over the tile sums (padded with +0
-// to a power of two), mean = S/N; V channel maximum over tiles, floored at
-// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv), D threads.
+// to P = a power of two), mean = S/N; V channel maximum over tiles, floored at
+// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv, D/32), 256 threads: a block
+// owns 32 columns, thread group g (8 of them) the chunks g, g+8, ... of C
+// consecutive tiles.  The tree over P leaves is the tree over the P/C aligned
+// chunk subtrees, so each thread builds whole chunk subtrees and the block
+// finishes the tree over the (at most 64) chunk sums level by level in LDS.
 // ---------------------------------------------------------------------------
-__global__ void prep_reduce_kernel(const PrepParams p) {
-    const int bh = blockIdx.x, d = threadIdx.x, D = p.D;
-    const int nk = p.nk;
+constexpr int kRedCols = 32;
+constexpr int kRedGroups = 8;
+
+// Pairwise tree over the C leaves (C a power of two, at most 16) of tiles
+// t0 .. t0+C-1; tiles >= nk are +0.
+__device__ __forceinline__ float chunk_tree16(const float *col, int D, int t0, int C, int nk) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = (k < C && t0 + k < nk) ? col[(int64_t)(t0 + k) * D] : 0.0f;
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) {
+        if (w < C) {
+#pragma unroll
+            for (int k = 0; k < w; ++k) v[k] = v[2 * k] + v[2 * k + 1];
+        }
+    }
+    return v[0];
+}
+
+// The same tree for any power of two C: the binary-counter evaluation (after
+// leaf i, ctz(i+1) merges of left + right) over 16-leaf subtrees.
+__device__ float chunk_tree(const float *col, int D, int t0, int C, int nk) {
+    if (C <= 16) return chunk_tree16(col, D, t0, C, nk);
+    float stack[32];
+    int top = 0;
+    const int n16 = C / 16;
+    for (int i = 0; i < n16; ++i) {
+        float x = chunk_tree16(col, D, t0 + 16 * i, 16, nk);
+        for (int m = __builtin_ctz((unsigned)(i + 1)); m > 0; --m) x = stack[--top] + x;
+        stack[top++] = x;
+    }
+    return stack[0];
+}
+
+__global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepParams p) {
+    __shared__ float tree[2][64][kRedCols + 1];
+    __shared__ float vmx[kRedGroups][kRedCols];
+    const int bh = blockIdx.x, D = p.D, nk = p.nk;
+    const int c = threadIdx.x % kRedCols, g = threadIdx.x / kRedCols;
+    const int d = blockIdx.y * kRedCols + c;
     const float *ks = p.ws_ksum + (int64_t)bh * nk * D + d;
     const float *vm = p.ws_vmax + (int64_t)bh * nk * D + d;
     int P = 1;
     while (P < nk) P <<= 1;
-    // Streaming evaluation of the balanced tree: after leaf i, merge the
-    // completed subtrees (ctz(i+1) merges); left subtree + right subtree.
-    float stack[32];
-    int top = 0;
-    for (int i = 0; i < P; ++i) {
-        float x = (i < nk) ? ks[(int64_t)i * D] : 0.0f;
-        for (int m = __builtin_ctz((unsigned)(i + 1)); m > 0; --m) x = stack[--top] + x;
-        stack[top++] = x;
-    }
-    p.k_mean[(int64_t)bh * D + d] = stack[0] / (float)p.N;
+    const int C = (P <= 1024) ? (P < 16 ? P : 16) : P / 64;   // tiles per chunk
+    const int NC = P / C;                                     // chunks, <= 64
     float m = 0.0f;
-    for (int i = 0; i < nk; ++i) m = __builtin_fmaxf(m, vm[(int64_t)i * D]);
-    const float amax = (m > 1e-7f) ? m : 1e-7f;
-    p.v_scale[(int64_t)bh * D + d] = amax / 2.25f;
-    p.ws_vamax[(int64_t)bh * D + d] = amax;
+    for (int j = g; j < NC; j += kRedGroups) {
+        tree[0][j][c] = chunk_tree(ks, D, j * C, C, nk);
+        const int te = min((j + 1) * C, nk);
+        for (int t = j * C; t < te; ++t) m = __builtin_fmaxf(m, vm[(int64_t)t * D]);
+    }
+    vmx[g][c] = m;
+    __syncthreads();
+    int src = 0;
+    for (int w = NC / 2; w >= 1; w >>= 1) {           // one tree level: left + right
+        for (int j = g; j < w; j += kRedGroups) tree[src ^ 1][j][c] = tree[src][2 * j][c] + tree[src][2 * j + 1][c];
+        src ^= 1;
+        __syncthreads();
+    }
+    if (g == 0) {
+        p.k_mean[(int64_t)bh * D + d] = tree[src][0][c] / (float)p.N;
+#pragma unroll
+        for (int i = 1; i < kRedGroups; ++i) m = __builtin_fmaxf(m, vmx[i][c]);
+        const float amax = (m > 1e-7f) ? m : 1e-7f;
+        p.v_scale[(int64_t)bh * D + d] = amax / 2.25f;
+        p.ws_vamax[(int64_t)bh * D + d] = amax;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2a: Q -> INT8, one scale per 32 rows.  Grid (q_rows/128, Hq, B); wave w
-// of block x owns group g = 4x + w (rows [32g, 32g+32)).
+// Pass 2a: Q -> INT8, one scale per 32 rows.  Grid (q_rows/128 * Hq, B),
+// x = (row block) * Hq + head; wave w of row block r owns group g = 4r + w
+// (rows [32g, 32g+32)).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
@@ -278,10 +330,10 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
     constexpr int NP = 32 / RPW;
     __shared__ __attribute__((aligned(16))) uint16_t ybuf[4][32 * D];
 
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.x % p.Hq, b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane % L, rr = lane / L;
-    const int g = blockIdx.x * 4 + wave;
+    const int g = (blockIdx.x / p.Hq) * 4 + wave;
     uint16_t *yb = ybuf[wave];
 
 #pragma unroll
@@ -327,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 
 // ---------------------------------------------------------------------------
 // Pass 2b: K -> subtract k_mean -> INT8, one scale per 64-row tile.
-// Grid (nk, Hkv, B).
+// Grid (nk * Hkv, B), x = tile * Hkv + head.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
@@ -337,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ybuf[64 * D];
     __shared__ float wmax[kThreads / 64];
 
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
 #pragma unroll
@@ -394,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
 // ---------------------------------------------------------------------------
 // Pass 2c: V -> E4M3 into tiles [D][64], keys of a tile in the slot order of
 // sage_v8_slot_key (the key order in which the attention kernel holds its
-// probabilities).  Grid (nk, Hkv, B).
+// probabilities).  Grid (nk * Hkv, B), x = tile * Hkv + head.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
@@ -403,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
     constexpr int NPASS = 64 / RPP;
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[64 * D];
 
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
@@ -440,18 +492,20 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
 using sage::PrepParams;
 
 hipError_t sage_launch_prep_stats(const PrepParams &p, hipStream_t s) {
-    dim3 grid(p.nk, p.Hkv, p.B);
+    // x = tile * H + head: concurrent work-groups read neighbouring heads of
+    // the same rows, i.e. long contiguous runs of an interleaved QKV row
+    const dim3 grid((unsigned)(p.nk * p.Hkv), p.B);
     if (p.D == 128) sage::prep_stats_kernel<128><<<grid, sage::kThreads, 0, s>>>(p);
     else sage::prep_stats_kernel<256><<<grid, sage::kThreads, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv), dim3(p.D), 0, s>>>(p);
+    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv, p.D / sage::kRedCols), 256, 0, s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t sage_launch_quant(const PrepParams &p, hipStream_t s) {
-    dim3 gq((unsigned)(p.q_rows / 128), p.Hq, p.B);
-    dim3 gk(p.nk, p.Hkv, p.B);
+    const dim3 gq((unsigned)(p.q_rows / 128 * p.Hq), p.B);
+    const dim3 gk((unsigned)(p.nk * p.Hkv), p.B);
     if (p.D == 128) {
         sage::quant_q_kernel<128><<<gq, sage::kThreads, 0, s>>>(p);
         sage::quant_k_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);

@@ -114,3 +114,13 @@ def test_batch_two_and_zero_rows():
     inp.k[0, 77] = 0           # a zero key row
     inp.v[:, :, 1, 9] = 0      # an all-zero V channel: amax floored at 1e-7
     _full_check(inp, "batch 2 with zero rows")
+
+
+@pytest.mark.timeout(600)
+def test_long_sequence_k_mean_tree():
+    # 1094 key tiles: the tree over tiles is padded to 2048 leaves, which the
+    # K-mean reduction builds from 32-tile chunk subtrees
+    inp = workloads.make_custom(1, 70001, 2, 2, 128, 96, seed=600)
+    rng = np.random.default_rng(42)
+    rows = _sample_rows(1, 2, 70001, 24, rng, tail=40)
+    _full_check(inp, "N=70001", attn_rows=rows)

@@ -64,6 +64,8 @@ def test_v8_slot_order_is_a_permutation(sage):
     (dict(rope_dim=95), "SAGE_E_ROPE"), (dict(rope_dim=130), "SAGE_E_ROPE"),
     (dict(rope_dim=-2), "SAGE_E_ROPE"), (dict(hadamard=True), "SAGE_E_UNSUPPORTED"),
     (dict(eps=0.0), "SAGE_E_UNSUPPORTED"), (dict(eps=float("nan")), "SAGE_E_UNSUPPORTED"),
+    # 4096 * 64 heads * 16384 key tiles = 2^32 work-groups in one launch
+    (dict(B=4096, Hq=64, Hkv=64, N=1 << 20), "SAGE_E_SHAPE"),
 ])
 def test_shape_refusals(sage, kw, err):
     base = dict(B=1, N=100, Hq=4, Hkv=2, D=128, rope_dim=96, hadamard=False, eps=1e-5)
@@ -120,3 +122,9 @@ def test_attn_refusals_happen_before_launch(sage):
     assert call(A, 0, 512, 256) == "SAGE_E_STRIDE"
     assert call(A + 8, 0, 512, 128) == "SAGE_E_ALIGN"
     assert call(A, 0, 512, 128, SageBufs(A, 0, A, A, A, A, A)) == "SAGE_E_NULL"
+
+
+def test_largest_grid_is_accepted(sage):
+    # 2^31 - 1 work-groups is the limit; just under it is accepted
+    z = sage.buffer_sizes(sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96))
+    assert z.n_k_tiles == 32767

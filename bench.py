@@ -121,6 +121,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        if ev is not None:
+            ev[2].record(stream)
         sage.prep(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
         sage.quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
         if ev is not None:
@@ -140,8 +142,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -149,8 +150,14 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    attn_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    prep_ms = sorted(e[2].elapsed_time(e[0]) for e in evs)
+    prep_avg_ms = sum(prep_ms) / len(prep_ms)
+    z = sage.buffer_sizes(shape)
+    # algorithmic prep bytes: read Q, K, V once (BF16), write q8, k8, v8 and the scales
+    prep_bytes = (2 * B * N * (Hq + 2 * Hkv) * D + B * N * (Hq + 2 * Hkv) * D
+                  + z.q_scale + z.k_scale + z.k_mean + z.v_scale)
     ms_step = elapsed * 1e3 / args.steps
 
     ops = cfg.attn_ops
@@ -183,6 +190,15 @@ def main():
             "avg_launch_ms": round(attn_avg_ms, 4),
             "median_launch_ms": round(attn_ms[len(attn_ms) // 2], 4),
             "ops_per_launch": ops,
+            "iqr_launch_ms": [round(attn_ms[len(attn_ms) // 4], 4), round(attn_ms[(3 * len(attn_ms)) // 4], 4)],
+            "min_launch_ms": round(attn_ms[0], 4),
+        },
+        "prep": {
+            "kernels": "sage_prep + sage_quant_qk (6 launches)",
+            "avg_ms": round(prep_avg_ms, 4),
+            "algorithmic_bytes": int(prep_bytes),
+            "GB_per_s": round(prep_bytes / (prep_avg_ms * 1e-3) / 1e9, 1),
+            "hbm_peak_GB_per_s": 8000.0,
         },
     }
     if not args.no_cpu_baseline:

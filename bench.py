@@ -11,7 +11,15 @@ Prints one JSON line:
   value      4*N^2*H*D / (step time)  [TFLOPS], whole path
   roofline   the attention kernel alone against the dense INT8/FP8 MFMA peak,
              timed with HIP events on the stream the kernel runs on
+  prep       sage_prep + sage_quant_qk time and their algorithmic HBM rate
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+
+--workload encoder instead times the short-encoder workload: 27 independent
+seeded layers of N=729, H=16, D=128, each prep + quant + attention, run (a) as
+27 back-to-back single-layer calls, (b) as the same calls captured once in a
+HIP graph and replayed, and (c) as one call with the layers stacked along the
+batch dimension (B = 27), which gives the attention launch 27x the
+work-groups of one layer.  All three must produce identical bytes.
 """
 from __future__ import annotations
 
@@ -85,6 +93,120 @@ def cpu_baseline(inp, cfg, budget_s: float = 12.0, heads=(0, 27, 55)):
     }
 
 
+def run_encoder(args):
+    """27 independent short-sequence layers: per-layer calls, a HIP graph of
+    them, and one stacked call.  One JSON line."""
+    import torch
+    import workloads
+    import quantized_exact_order_amd as sage
+
+    cfg = workloads.CONFIGS["encoder"]
+    L, N, H, D = 27, cfg.N, cfg.Hq, cfg.D
+    print(f"[bench] generating {L} encoder layers N={N} H={H} D={D}", file=sys.stderr, flush=True)
+    layers = [workloads.make_inputs(cfg, layer=l) for l in range(L)]
+    for x in layers[1:]:
+        assert torch.equal(x.w_q, layers[0].w_q) and torch.equal(x.w_k, layers[0].w_k)
+    dev = torch.device("cuda:0")
+    q = torch.cat([x.q for x in layers]).to(dev)             # [L, N, H, D], layer = batch row
+    k = torch.cat([x.k for x in layers]).to(dev)
+    v = torch.cat([x.v for x in layers]).to(dev)
+    w_q, w_k = layers[0].w_q.to(dev), layers[0].w_k.to(dev)
+    cos, sin = layers[0].cos.to(dev).contiguous(), layers[0].sin.to(dev).contiguous()
+    one = sage.Shape(1, N, H, H, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+    stacked = sage.Shape(L, N, H, H, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+    bufs1 = [sage.Buffers.allocate(one, dev) for _ in range(L)]
+    o1 = torch.empty((L, N, H, D), dtype=torch.bfloat16, device=dev)
+    bufsL = sage.Buffers.allocate(stacked, dev)
+    oL = torch.empty((L, N, H, D), dtype=torch.bfloat16, device=dev)
+
+    def per_layer():
+        st = torch.cuda.current_stream()
+        for l in range(L):
+            a = (q[l:l + 1], k[l:l + 1], v[l:l + 1], w_q, w_k, cos, sin, st)
+            sage.prep(one, bufs1[l], *a)
+            sage.quant_qk(one, bufs1[l], *a)
+            sage.attn_fwd(one, bufs1[l], o1[l:l + 1], st)
+
+    attn_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def batched(ev=False):
+        st = torch.cuda.current_stream()
+        a = (q, k, v, w_q, w_k, cos, sin, st)
+        sage.prep(stacked, bufsL, *a)
+        sage.quant_qk(stacked, bufsL, *a)
+        if ev:
+            attn_ev[0].record(st)
+        sage.attn_fwd(stacked, bufsL, oL, st)
+        if ev:
+            attn_ev[1].record(st)
+
+    # graph of the per-layer sequence (captured after an eager warmup)
+    per_layer()
+    torch.cuda.synchronize()
+    ref = o1.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        per_layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        per_layer()
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(args.steps, 1)
+    print(f"[bench] timing {reps} runs of each mode", file=sys.stderr, flush=True)
+    t_layers = timed(per_layer, reps)
+    o1.zero_()
+    t_graph = timed(graph.replay, reps)
+    graph_ok = bool(torch.equal(o1.view(torch.int16), ref.view(torch.int16)))
+    t_batched = timed(batched, reps)
+    batched_ok = bool(torch.equal(oL.view(torch.int16), ref.view(torch.int16)))
+    attn_ms = []
+    for _ in range(reps):
+        batched(ev=True)
+        torch.cuda.synchronize()
+        attn_ms.append(attn_ev[0].elapsed_time(attn_ev[1]))
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    if not (graph_ok and batched_ok):
+        print("[bench] encoder modes disagree", file=sys.stderr, flush=True)
+        sys.exit(1)
+    ops = L * 4 * N * N * H * D
+    best = min(t_layers, t_graph, t_batched)
+    result = {
+        "metric": "encoder attention TFLOPS (27 layers x 4*N^2*H*D / t) at N=729,H=16,D=128",
+        "value": round(ops / (best * 1e-3) / 1e12, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(best, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+e4m3", "data": "synthetic",
+        "config": {"workload": "short encoder: 27 independent seeded layers, B=1 N=729 H=16 D=128 each, "
+                               "prep + quant + attention per layer",
+                   "layers": L, "N": N, "H": H, "D": D},
+        "modes_ms_per_27_layers": {"per_layer_calls": round(t_layers, 4),
+                                   "per_layer_calls_hip_graph": round(t_graph, 4),
+                                   "stacked_batch_27": round(t_batched, 4)},
+        "stacked_attention_launch_ms": round(attn_avg, 4),
+        "stacked_attention_frac_of_peak": round(ops / (attn_avg * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "outputs_identical_across_modes": True,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,12 +215,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
+    ap.add_argument("--workload", choices=("canonical", "encoder"), default="canonical")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
               "shards by head with no exchange, so one GPU's throughput is the measured figure.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "encoder":
+        return run_encoder(args)
 
     import torch
     import workloads

@@ -68,6 +68,9 @@ def lib():
         L.oracle_quant_k.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
         L.oracle_quant_v.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
         L.oracle_attn_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P]
+        L.oracle_attn_rows_mode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P, i32]
+        L.oracle_f64_to_f16.restype = f32
+        L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = i32
         for name in ("oracle_f32_to_bf16_n", "oracle_f32_to_e4m3_n", "oracle_f32_to_i8_n",
                      "oracle_exp2_n"):
@@ -236,18 +239,25 @@ def prepare(inp, rope_dim: Optional[int] = None, hadamard: Optional[bool] = None
     return Prepared(zq, zk, mean, q8, qs, k8, ks, v8, vs)
 
 
-def attn_rows(p: Prepared, rows: np.ndarray) -> np.ndarray:
-    """Quantized attention output (uint16 BF16 [len(rows), D]) for rows (b, h, i)."""
+def attn_rows(p: Prepared, rows: np.ndarray, pv_fp16: bool = False) -> np.ndarray:
+    """Quantized attention output (uint16 BF16 [len(rows), D]) for rows (b, h, i).
+
+    pv_fp16 selects the emulation of the page's two-level PV accumulation
+    (FP16 per-tile partial) instead of the FP32 per-tile partial."""
     B, Hq, N, D = p.q8.shape
     Hkv = p.k8.shape[1]
     rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 3)
     o = np.empty((rows.shape[0], D), np.uint16)
     if rows.shape[0] == 0:
         return o
-    lib().oracle_attn_rows(B, N, Hq, Hkv, D, _ptr(p.q8), _ptr(p.q_scale), _ptr(p.k8),
-                           _ptr(p.k_scale), _ptr(p.v8), _ptr(p.v_scale), rows.shape[0],
-                           _ptr(rows), _ptr(o))
+    lib().oracle_attn_rows_mode(B, N, Hq, Hkv, D, _ptr(p.q8), _ptr(p.q_scale), _ptr(p.k8),
+                                _ptr(p.k_scale), _ptr(p.v8), _ptr(p.v_scale), rows.shape[0],
+                                _ptr(rows), _ptr(o), int(bool(pv_fp16)))
     return o
+
+
+def f64_to_f16(x: float) -> float:
+    return float(lib().oracle_f64_to_f16(float(x)))
 
 
 def all_rows(B: int, H: int, N: int) -> np.ndarray:
@@ -255,10 +265,10 @@ def all_rows(B: int, H: int, N: int) -> np.ndarray:
     return np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int32)
 
 
-def attention(p: Prepared) -> np.ndarray:
+def attention(p: Prepared, pv_fp16: bool = False) -> np.ndarray:
     """Full quantized attention output as uint16 BF16 [B,N,Hq,D]."""
     B, Hq, N, D = p.q8.shape
-    o = attn_rows(p, all_rows(B, Hq, N))
+    o = attn_rows(p, all_rows(B, Hq, N), pv_fp16)
     return o.reshape(B, Hq, N, D).transpose(0, 2, 1, 3).copy()
 
 

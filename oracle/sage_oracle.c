@@ -125,6 +125,27 @@ float oracle_score_scale(int D)
 /* Preparation                                                               */
 /* ------------------------------------------------------------------------ */
 
+/*
+ * RNE rounding of a real (held exactly in a double) to IEEE binary16: 10
+ * fraction bits, exponent range [-14, 15], subnormal quantum 2^-24, values
+ * at or above 65520 become infinity.  Returned as the float of that binary16
+ * value (every binary16 value is a float).
+ * Pinned by: numpy's float64 -> float16 conversion over random, tie and
+ * subnormal inputs.
+ */
+float oracle_f64_to_f16(double x)
+{
+    if (x == 0.0 || x != x) return (float)x;
+    double ax = fabs(x);
+    if (ax >= 65520.0) return x > 0 ? INFINITY : -INFINITY;
+    int e2;
+    frexp(ax, &e2);                      /* ax = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;                      /* ax in [2^E, 2^(E+1)) */
+    double quantum = (E < -14) ? ldexp(1.0, -24) : ldexp(1.0, E - 10);
+    double r = rint(ax / quantum) * quantum;   /* exact division by a power of two */
+    return (float)(x < 0 ? -r : r);
+}
+
 /* In-place balanced pairwise sum over n (a power of two) in natural order:
  * each level adds neighbours (t[2i], t[2i+1]). */
 static float pairwise_sum(float *t, int n)
@@ -391,15 +412,17 @@ void oracle_quant_v(int B, int N, int H, int D, const uint16_t *v, int64_t sb, i
  * then O[e] = bf16((RO[e] * (1.0f / d)) * v_scale[e]).
  *
  * The per-tile FP32 sum T stands for the page's per-tile PV partial, which it
- * accumulates in FP16 on its hardware; the oracle keeps FP32 (reading).
+ * accumulates in FP16 on its hardware; the oracle keeps FP32 (reading), and
+ * oracle_attn_rows_mode(..., pv_fp16 = 1) emulates the FP16 two-level
+ * accumulation instead.
  * Pinned by: N=1 and zero-query closed forms, one-hot rows, FP64 softmax
  * attention (cosine), brute-force integer dot products.
  */
-void oracle_attn_rows(int B, int N, int Hq, int Hkv, int D,
-                      const int8_t *q8, const float *q_scale,
-                      const int8_t *k8, const float *k_scale,
-                      const uint8_t *v8, const float *v_scale,
-                      int64_t nrows, const int32_t *rows, uint16_t *o)
+void oracle_attn_rows_mode(int B, int N, int Hq, int Hkv, int D,
+                           const int8_t *q8, const float *q_scale,
+                           const int8_t *k8, const float *k_scale,
+                           const uint8_t *v8, const float *v_scale,
+                           int64_t nrows, const int32_t *rows, uint16_t *o, int pv_fp16)
 {
     const int nq = ((N + 127) / 128) * 4;
     const int nk = (N + 63) / 64;
@@ -453,13 +476,32 @@ void oracle_attn_rows(int B, int N, int Hq, int Hkv, int D,
                 d = d + p;
                 p8[j] = oracle_f32_to_e4m3(p);
             }
-            for (int e = 0; e < D; e++) T[e] = 0.0f;
-            for (int j = 0; j < 64; j++) {
-                int key = t * 64 + j;
-                if (key >= N) continue;           /* invalid V rows are zero */
-                float pj = dec[p8[j]];
-                const uint8_t *vr = vb + (int64_t)key * D;
-                for (int e = 0; e < D; e++) T[e] = T[e] + pj * dec[vr[e]];
+            if (!pv_fp16) {
+                for (int e = 0; e < D; e++) T[e] = 0.0f;
+                for (int j = 0; j < 64; j++) {
+                    int key = t * 64 + j;
+                    if (key >= N) continue;           /* invalid V rows are zero */
+                    float pj = dec[p8[j]];
+                    const uint8_t *vr = vb + (int64_t)key * D;
+                    for (int e = 0; e < D; e++) T[e] = T[e] + pj * dec[vr[e]];
+                }
+            } else {
+                /* two ordered K=32 steps into an FP16 fragment: each step adds
+                 * its 32 exact products (exact in double) to the fragment and
+                 * rounds once to FP16 */
+                for (int e = 0; e < D; e++) {
+                    double frag = 0.0;
+                    for (int half = 0; half < 2; half++) {
+                        double acc = frag;
+                        for (int j = 32 * half; j < 32 * half + 32; j++) {
+                            int key = t * 64 + j;
+                            if (key >= N) continue;
+                            acc += (double)dec[p8[j]] * (double)dec[vb[(int64_t)key * D + e]];
+                        }
+                        frag = (double)oracle_f64_to_f16(acc);
+                    }
+                    T[e] = (float)frag;
+                }
             }
             for (int e = 0; e < D; e++) RO[e] = RO[e] + T[e];
             m = mn;
@@ -472,6 +514,19 @@ void oracle_attn_rows(int B, int N, int Hq, int Hkv, int D,
 }
 
 /* Number of OpenMP threads the oracle runs with (for reporting). */
+/* The FP32 per-tile partial (pv_fp16 = 0) is the oracle's reading and the
+ * parity target; pv_fp16 = 1 emulates the page's two-level PV (each 64-key
+ * partial accumulated in FP16 by two ordered K=32 steps, then added to the
+ * FP32 RO) to measure how far an FP32-accumulating path sits from it. */
+void oracle_attn_rows(int B, int N, int Hq, int Hkv, int D,
+                      const int8_t *q8, const float *q_scale,
+                      const int8_t *k8, const float *k_scale,
+                      const uint8_t *v8, const float *v_scale,
+                      int64_t nrows, const int32_t *rows, uint16_t *o)
+{
+    oracle_attn_rows_mode(B, N, Hq, Hkv, D, q8, q_scale, k8, k_scale, v8, v_scale, nrows, rows, o, 0);
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -124,3 +124,22 @@ def test_long_sequence_k_mean_tree():
     rng = np.random.default_rng(42)
     rows = _sample_rows(1, 2, 70001, 24, rng, tail=40)
     _full_check(inp, "N=70001", attn_rows=rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail"])
+def test_fp32_accumulation_is_closer_to_fp32_reading_than_to_fp16_partials(name):
+    # the GPU's FP8 MFMA accumulates each tile's PV in FP32; the page's kernel
+    # accumulates it in FP16 (emulated by the oracle): the GPU output must sit
+    # nearer the oracle's FP32 reading
+    inp = workloads.make_inputs(workloads.CONFIGS[name])
+    banner(f"{name}: GPU vs oracle FP32 / FP16 PV partials")
+    ref = oracle.prepare(inp)
+    _, _, o = run_path(inp)
+    g = oracle.bf16_to_f32(bf16_bits(o)).astype(np.float64)
+    a = oracle.bf16_to_f32(oracle.attention(ref)).astype(np.float64)
+    b = oracle.bf16_to_f32(oracle.attention(ref, pv_fp16=True)).astype(np.float64)
+    da, db = np.abs(g - a), np.abs(g - b)
+    print(f"[gpu] {name}: vs FP32 reading max-abs {da.max():.3g} differing {np.mean(g != a):.4f}; "
+          f"vs FP16 partials max-abs {db.max():.3g} differing {np.mean(g != b):.4f}", flush=True)
+    assert np.mean(g != a) < np.mean(g != b)
+    assert 1.0 - oracle.cosine(g, a) < 1.0 - oracle.cosine(g, b)

@@ -110,3 +110,21 @@ def test_score_scale_is_log2e_over_sqrt_d(oracle_lib, D):
     assert abs(c * math.sqrt(D) * math.log(2.0) - 1.0) < 2.0**-23
     expected_bits = {128: 0x3E0293EE, 256: 0x3DB8AA3B}[D]
     assert np.float32(c).view(np.uint32) == expected_bits
+
+
+def test_f16_rounding_matches_numpy():
+    import oracle
+    rng = np.random.default_rng(3)
+    # every binary16 value, the midpoints between neighbours (ties) and their
+    # neighbours in double, plus random doubles over the whole range
+    h = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (h[:-1] + h[1:]) / 2
+    xs = np.concatenate([h, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                         rng.uniform(-70000, 70000, 4000), rng.standard_normal(4000) * 1e-5,
+                         [65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25]])
+    xs = np.concatenate([xs, -xs])
+    mine = np.array([oracle.f64_to_f16(x) for x in xs], np.float64)
+    with np.errstate(over="ignore"):              # values >= 65520 become inf, as in the oracle
+        ref = xs.astype(np.float16).astype(np.float64)
+    same = (mine == ref) | (np.isinf(mine) & np.isinf(ref) & (np.sign(mine) == np.sign(ref)))
+    assert same.all(), xs[~same][:5]

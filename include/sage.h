@@ -147,6 +147,52 @@ sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, cons
 sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
                           int64_t osn, int64_t osh, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Decode-time INT8 K cache (the NPU issue page on INT8 KV with per-head
+ * Hadamard rotation, part A, the variant with INT8 K and 16-bit V): every K
+ * row is multiplied by the normalized Walsh-Hadamard matrix and stored as
+ * INT8 with one FP32 scale per (head, token); the query is rotated by the
+ * same matrix, which leaves every score unchanged because the matrix is
+ * orthogonal.  V is kept in BF16.  Head width D = 256 only.
+ * ------------------------------------------------------------------------ */
+
+/* The cache, owned by the caller (device memory, 16-byte aligned):
+ *   k8       INT8 [B, Hkv, capacity, D]  rotated K rows
+ *   k_scale  FP32 [B, Hkv, capacity]     amax / 127 of each rotated row
+ *   v        BF16 [B, Hkv, capacity, D]  V rows                             */
+typedef struct sage_kv_cache {
+    int8_t *k8;
+    float *k_scale;
+    uint16_t *v;
+    int32_t B, Hkv, D, capacity;
+} sage_kv_cache;
+
+/* Writes n new tokens at cache positions [t0, t0 + n): per row (b, t, h) of
+ * the BF16 views k and v ([B, n, Hkv, D], unit d stride, 16-byte aligned
+ * rows), u = H k / 16, k_scale = max(1e-7, max|u|) / 127,
+ * k8 = round-half-even-saturate(u * (127 / max(1e-7, max|u|))), v copied.
+ * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256), SAGE_E_SHAPE
+ * (B, Hkv, n < 1, t0 < 0 or t0 + n > capacity), SAGE_E_STRIDE,
+ * SAGE_E_ALIGN, SAGE_E_HIP. */
+sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, const sage_view_bf16 *v,
+                           int32_t t0, int32_t n, void *stream);
+
+/* Workspace bytes of sage_decode_attn for Hq query heads over T tokens. */
+sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_t T, size_t *bytes);
+
+/* Single-query attention of each of the Hq query heads (view q [B, 1, Hq, D])
+ * over cache positions [0, T) of KV head h / (Hq / Hkv):
+ *   s_t = ((H q / 16) . k8_t) * k_scale_t / 16,  w = softmax(s),
+ *   o = bf16(sum_t w_t v_t)                     (FP32 on the GPU)
+ * o: BF16 [B, Hq, D] contiguous.  The cache is read once: the work-group of
+ * one KV head and 256 tokens serves its Hq / Hkv query heads, and the chunk
+ * partials are combined in increasing token order (deterministic).
+ * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256, Hq / Hkv not 1, 2,
+ * 4, 8 or 16), SAGE_E_GQA, SAGE_E_SHAPE (T < 1 or T > capacity),
+ * SAGE_E_STRIDE, SAGE_E_ALIGN, SAGE_E_WORKSPACE, SAGE_E_HIP. */
+sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
+                             void *o, void *workspace, size_t ws_bytes, void *stream);
+
 /* Key (0..63, within its tile) stored at position `slot` (0..63) of every
  * channel row of a v8 tile; -1 if slot is out of range. */
 int32_t sage_v8_key_of_slot(int32_t slot);

@@ -69,6 +69,8 @@ def lib():
         L.oracle_quant_v.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
         L.oracle_attn_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P]
         L.oracle_attn_rows_mode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P, i32]
+        L.oracle_kv_quant.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
+        L.oracle_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_f64_to_f16.restype = f32
         L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = i32
@@ -317,3 +319,38 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()
     return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+# ----------------------------------------------------------------------------
+# Decode-time INT8 K cache (per-head Hadamard rotation, one scale per token)
+# ----------------------------------------------------------------------------
+
+def kv_quant(k: torch.Tensor):
+    """Cache entries of BF16 K rows k [B, T, H, D] (CPU tensor, any strides,
+    unit d stride): (k8 int8 [B, H, T, D], kscale float32 [B, H, T])."""
+    B, T, H, D = k.shape
+    if k.stride(3) != 1:
+        k = k.contiguous()
+    k8 = np.empty((B, H, T, D), np.int8)
+    ks = np.empty((B, H, T), np.float32)
+    sb, sn, sh, _ = k.stride()
+    lib().oracle_kv_quant(B, T, H, D, ctypes.c_void_p(k.data_ptr()), sb, sn, sh, _ptr(k8), _ptr(ks))
+    return k8, ks
+
+
+def decode_attn(q: torch.Tensor, k8: np.ndarray, kscale: np.ndarray, v_cache: np.ndarray, T: int):
+    """Single-query attention over the first T cached tokens.
+    q BF16 [B, Hq, D]; k8 [B, Hkv, Tc, D]; kscale [B, Hkv, Tc]; v_cache BF16
+    bits uint16 [B, Hkv, Tc, D].  Returns (o uint16 BF16 [B, Hq, D],
+    weights float64 [B, Hq, T])."""
+    B, Hq, D = q.shape
+    Hkv, Tc = k8.shape[1], k8.shape[2]
+    qb = np.ascontiguousarray(q.contiguous().view(torch.int16).numpy().view(np.uint16))
+    k8 = np.ascontiguousarray(k8)
+    kscale = np.ascontiguousarray(kscale, np.float32)
+    v_cache = np.ascontiguousarray(v_cache, np.uint16)
+    o = np.empty((B, Hq, D), np.uint16)
+    w = np.empty((B, Hq, max(T, 1)), np.float64)
+    lib().oracle_decode_attn(B, Hq, Hkv, D, T, Tc, _ptr(qb), _ptr(k8), _ptr(kscale), _ptr(v_cache),
+                             _ptr(o), _ptr(w))
+    return o, w[:, :, :T]

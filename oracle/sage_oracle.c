@@ -527,6 +527,99 @@ void oracle_attn_rows(int B, int N, int Hq, int Hkv, int D,
     oracle_attn_rows_mode(B, N, Hq, Hkv, D, q8, q_scale, k8, k_scale, v8, v_scale, nrows, rows, o, 0);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Decode-time INT8 K cache with per-head Hadamard rotation                  */
+/* (the NPU issue page on INT8 KV with per-head Hadamard rotation, part A:   */
+/* INT8 K with one FP32 scale per (head, token) taken after the rotation;    */
+/* the rotation is free on the K side because (QH)(KH)^T = QK^T; V stays in  */
+/* 16-bit floating point)                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Cache entry of K row (b, t, h) of a BF16 view with element strides
+ * (sb, sn, sh) and unit d stride:
+ *   u     = oracle_wht(float(k))             (normalized, FP32 stages)
+ *   amax  = max(1e-7, max_d |u|);  scale = amax / 127
+ *   k8    = i8(u * (127 / amax))             (own division, RNE, saturating)
+ * Writes k8 [B, H, T, D] and kscale [B, H, T].  The quantization formula is
+ * the one the contract page gives for Q and K blocks, applied to one row.
+ * Pinned by: |u - k8 * scale| <= scale / 2 and max |k8| = 127 per row, and the
+ * rotated scores against scipy's Hadamard matrix.
+ */
+void oracle_kv_quant(int B, int T, int H, int D, const uint16_t *k, int64_t sb, int64_t sn,
+                     int64_t sh, int8_t *k8, float *kscale)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++) {
+            float *u = (float *)malloc(sizeof(float) * D);
+            for (int t = 0; t < T; t++) {
+                const uint16_t *row = k + (int64_t)b * sb + (int64_t)t * sn + (int64_t)h * sh;
+                for (int d = 0; d < D; d++) u[d] = oracle_bf16_to_f32(row[d]);
+                oracle_wht(u, D);
+                int64_t r = ((int64_t)b * H + h) * T + t;
+                kscale[r] = quant_group(u, 1, D, k8 + r * D);
+            }
+            free(u);
+        }
+}
+
+/*
+ * Single-query attention of query row (b, h) over the first T cached tokens
+ * of KV head h / (Hq / Hkv), in FP64 (the page fixes the cache formats, not
+ * the arithmetic of the decode step; FP64 is the plain reading):
+ *   qr   = oracle_wht(float(q))                        (FP32, as the cache)
+ *   s_t  = (sum_d qr[d] * k8[t, d]) * kscale[t] / sqrt(D)
+ *   w    = softmax(s) over t < T
+ *   o[d] = sum_t w_t * float(v[t, d]);  O = bf16(float(o))
+ * q: BF16 [B, Hq, D]; k8 [B, Hkv, Tc, D], kscale [B, Hkv, Tc], v: BF16
+ * [B, Hkv, Tc, D] (cache capacity Tc >= T); o: BF16 [B, Hq, D]; w (optional):
+ * FP64 [B, Hq, T] attention weights.
+ * Pinned by: numpy attention on the dequantized cache rotated back with
+ * scipy's Hadamard matrix, T = 1 closed form, uniform weights for a zero query.
+ */
+void oracle_decode_attn(int B, int Hq, int Hkv, int D, int T, int Tc, const uint16_t *q,
+                        const int8_t *k8, const float *kscale, const uint16_t *v, uint16_t *o,
+                        double *w)
+{
+    const int grp = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hq; h++) {
+            const int hk = h / grp;
+            float *qr = (float *)malloc(sizeof(float) * D);
+            double *s = (double *)malloc(sizeof(double) * (T > 0 ? T : 1));
+            double *acc = (double *)calloc(D, sizeof(double));
+            const uint16_t *qrow = q + ((int64_t)b * Hq + h) * D;
+            for (int d = 0; d < D; d++) qr[d] = oracle_bf16_to_f32(qrow[d]);
+            oracle_wht(qr, D);
+            const int64_t base = ((int64_t)b * Hkv + hk) * Tc;
+            double mx = -INFINITY;
+            for (int t = 0; t < T; t++) {
+                double dot = 0.0;
+                const int8_t *kr = k8 + (base + t) * D;
+                for (int d = 0; d < D; d++) dot += (double)qr[d] * (double)kr[d];
+                s[t] = dot * (double)kscale[base + t] / sqrt((double)D);
+                if (s[t] > mx) mx = s[t];
+            }
+            double l = 0.0;
+            for (int t = 0; t < T; t++) {
+                s[t] = exp(s[t] - mx);
+                l += s[t];
+            }
+            for (int t = 0; t < T; t++) {
+                const double wt = s[t] / l;
+                if (w) w[((int64_t)b * Hq + h) * T + t] = wt;
+                const uint16_t *vr = v + (base + t) * D;
+                for (int d = 0; d < D; d++) acc[d] += wt * (double)oracle_bf16_to_f32(vr[d]);
+            }
+            for (int d = 0; d < D; d++) o[((int64_t)b * Hq + h) * D + d] = oracle_f32_to_bf16((float)acc[d]);
+            free(qr);
+            free(s);
+            free(acc);
+        }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

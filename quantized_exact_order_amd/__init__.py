@@ -9,6 +9,12 @@ quantization, attention) runs in the library's HIP kernels.
     prep(shape, bufs, q, k, v, w_q, w_k, cos, sin)       # pass 1
     quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin)   # pass 2
     o = attn_fwd(shape, bufs)                            # BF16 [B, N, Hq, D]
+
+Decode-time INT8 K cache (per-head Hadamard rotation, one scale per token):
+
+    cache = KvCache.allocate(B, Hkv, capacity, device)   # D = 256
+    kv_append(cache, k, v, t0)                           # k, v BF16 [B, n, Hkv, D]
+    o = decode_attn(cache, q, T)                         # q BF16 [B, Hq, D] -> [B, Hq, D]
 """
 from __future__ import annotations
 
@@ -18,11 +24,12 @@ from typing import Optional
 
 import torch
 
-from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageShape, SageSizes, SageView,
-                   check, lib)
+from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageKvCache, SageShape, SageSizes,
+                   SageView, check, lib)
 
 __all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
-           "v8_logical", "v8_slot_keys", "SageError", "LIB_PATH", "EXPORTS"]
+           "v8_logical", "v8_slot_keys", "KvCache", "kv_append", "decode_workspace", "decode_attn",
+           "SageError", "LIB_PATH", "EXPORTS"]
 
 
 @dataclass(frozen=True)
@@ -151,3 +158,58 @@ def v8_logical(shape: Shape, bufs: Buffers) -> torch.Tensor:
     inv[keys] = torch.arange(64, device=keys.device)
     t = bufs.v8.index_select(4, inv)                      # [B,Hkv,nk,D,64] in key order
     return t.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nk * 64, D)[:, :, :shape.N]
+
+
+# ----------------------------------------------------------------------------
+# Decode-time INT8 K cache
+# ----------------------------------------------------------------------------
+
+@dataclass
+class KvCache:
+    """Device tensors behind sage_kv_cache (D = 256)."""
+    k8: torch.Tensor         # int8  [B, Hkv, capacity, D], rotated K rows
+    k_scale: torch.Tensor    # f32   [B, Hkv, capacity]
+    v: torch.Tensor          # bf16  [B, Hkv, capacity, D]
+
+    @classmethod
+    def allocate(cls, B: int, Hkv: int, capacity: int, device, D: int = 256) -> "KvCache":
+        return cls(torch.zeros((B, Hkv, capacity, D), dtype=torch.int8, device=device),
+                   torch.zeros((B, Hkv, capacity), dtype=torch.float32, device=device),
+                   torch.zeros((B, Hkv, capacity, D), dtype=torch.bfloat16, device=device))
+
+    def c(self) -> SageKvCache:
+        B, Hkv, cap, D = self.k8.shape
+        return SageKvCache(self.k8.data_ptr(), self.k_scale.data_ptr(), self.v.data_ptr(),
+                           B, Hkv, D, cap)
+
+
+def kv_append(cache: KvCache, k, v, t0: int, stream=None) -> None:
+    """Rotate, quantize and store K (BF16 [B, n, Hkv, D]) and copy V at
+    positions [t0, t0 + n) (sage_kv_append)."""
+    kv, vv = _view(k, "k"), _view(v, "v")
+    check(lib.sage_kv_append(ctypes.byref(cache.c()), ctypes.byref(kv), ctypes.byref(vv), t0,
+                             k.shape[1], _stream(stream)), "sage_kv_append")
+
+
+def decode_workspace(cache: KvCache, Hq: int, T: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib.sage_decode_workspace(ctypes.byref(cache.c()), Hq, T, ctypes.byref(n)), "sage_decode_workspace")
+    return n.value
+
+
+def decode_attn(cache: KvCache, q, T: int, o: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Single-query attention of q (BF16 [B, Hq, D]) over cache positions
+    [0, T) (sage_decode_attn); returns BF16 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    if o is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, D) or not o.is_contiguous():
+        raise ValueError("o must be a contiguous BF16 [B, Hq, D] tensor")
+    need = decode_workspace(cache, Hq, T)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    qv = _view(q.unsqueeze(1), "q")
+    check(lib.sage_decode_attn(ctypes.byref(cache.c()), Hq, ctypes.byref(qv), T, o.data_ptr(),
+                               workspace.data_ptr(), workspace.numel(), _stream(stream)), "sage_decode_attn")
+    return o

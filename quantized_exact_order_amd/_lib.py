@@ -47,6 +47,11 @@ class SageSizes(ctypes.Structure):
                 ("q_rows", i64), ("n_q_groups", i64), ("k_rows", i64), ("n_k_tiles", i64)]
 
 
+class SageKvCache(ctypes.Structure):
+    _fields_ = [("k8", vp), ("k_scale", vp), ("v", vp), ("B", i32), ("Hkv", i32), ("D", i32),
+                ("capacity", i32)]
+
+
 P = ctypes.POINTER
 _lib.sage_buffer_sizes.argtypes = [P(SageShape), P(SageSizes)]
 _lib.sage_buffer_sizes.restype = i32
@@ -57,6 +62,12 @@ for _name in ("sage_prep", "sage_quant_qk"):
     fn.restype = i32
 _lib.sage_attn_fwd.argtypes = [P(SageShape), P(SageBufs), vp, i64, i64, i64, vp]
 _lib.sage_attn_fwd.restype = i32
+_lib.sage_kv_append.argtypes = [P(SageKvCache), P(SageView), P(SageView), i32, i32, vp]
+_lib.sage_kv_append.restype = i32
+_lib.sage_decode_workspace.argtypes = [P(SageKvCache), i32, i32, P(sz)]
+_lib.sage_decode_workspace.restype = i32
+_lib.sage_decode_attn.argtypes = [P(SageKvCache), i32, P(SageView), i32, vp, vp, sz, vp]
+_lib.sage_decode_attn.restype = i32
 _lib.sage_v8_key_of_slot.argtypes = [i32]
 _lib.sage_v8_key_of_slot.restype = i32
 _lib.sage_status_str.argtypes = [i32]
@@ -64,6 +75,7 @@ _lib.sage_status_str.restype = ctypes.c_char_p
 _lib.sage_version.restype = i32
 
 EXPORTS = ("sage_buffer_sizes", "sage_prep", "sage_quant_qk", "sage_attn_fwd",
+           "sage_kv_append", "sage_decode_workspace", "sage_decode_attn",
            "sage_v8_key_of_slot", "sage_status_str", "sage_version")
 
 

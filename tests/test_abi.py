@@ -128,3 +128,35 @@ def test_largest_grid_is_accepted(sage):
     # 2^31 - 1 work-groups is the limit; just under it is accepted
     z = sage.buffer_sizes(sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96))
     assert z.n_k_tiles == 32767
+
+
+def test_decode_cache_refusals_happen_before_launch(sage):
+    from quantized_exact_order_amd._lib import lib, SageKvCache, SageView, STATUS_NAMES
+    A = 0x100000
+    name = lambda st: STATUS_NAMES[st]
+    cache = lambda **kw: SageKvCache(**{**dict(k8=A, k_scale=A, v=A, B=1, Hkv=2, D=256, capacity=64), **kw})
+    kv = SageView(A, 0, 2 * 256, 256, 1)
+    append = lambda c, t0, n, k=kv: name(lib.sage_kv_append(ctypes.byref(c), ctypes.byref(k), ctypes.byref(kv),
+                                                            t0, n, None))
+    assert append(cache(k8=0), 0, 1) == "SAGE_E_NULL"
+    assert append(cache(D=128), 0, 1) == "SAGE_E_UNSUPPORTED"
+    assert append(cache(), 60, 5) == "SAGE_E_SHAPE"            # past the capacity
+    assert append(cache(), -1, 1) == "SAGE_E_SHAPE"
+    assert append(cache(), 0, 0) == "SAGE_E_SHAPE"
+    assert append(cache(v=A + 4), 0, 1) == "SAGE_E_ALIGN"
+    assert append(cache(), 0, 1, SageView(A, 0, 512, 256, 2)) == "SAGE_E_STRIDE"
+    n = ctypes.c_size_t()
+    assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 64, ctypes.byref(n))) == "SAGE_OK"
+    assert n.value == 1 * 8 * 1 * 258 * 4 + (-(1 * 8 * 258 * 4) % 256)
+    assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 65, ctypes.byref(n))) == "SAGE_E_SHAPE"
+    q = SageView(A, 0, 8 * 256, 256, 1)
+    attn = lambda c, Hq, T, ws=A, wsb=1 << 30, o=A: name(lib.sage_decode_attn(
+        ctypes.byref(c), Hq, ctypes.byref(q), T, o, ws, wsb, None))
+    assert attn(cache(), 8, 64, o=None) == "SAGE_E_NULL"
+    assert attn(cache(), 7, 64) == "SAGE_E_GQA"
+    assert attn(cache(), 6, 64) == "SAGE_E_UNSUPPORTED"       # 3 query heads per KV head
+    assert attn(cache(), 8, 0) == "SAGE_E_SHAPE"
+    assert attn(cache(), 8, 65) == "SAGE_E_SHAPE"
+    assert attn(cache(), 8, 64, wsb=16) == "SAGE_E_WORKSPACE"
+    assert attn(cache(), 8, 64, ws=0) == "SAGE_E_WORKSPACE"
+    assert attn(cache(), 8, 64, o=A + 8) == "SAGE_E_ALIGN"

@@ -1,0 +1,133 @@
+"""Decode-time INT8 K cache on the GPU against the oracle: the cache (rotated
+INT8 K, per-(head, token) scales, BF16 V) byte-identical, the single-query
+attention within the rounding of an FP32 evaluation (at most one or two BF16
+steps of the output, cosine 0.99999), and the KL-divergence gate of the NPU
+issue page on the GPU-written cache."""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from gpu_util import banner
+
+pytestmark = pytest.mark.gpu
+
+D = 256
+HM = scipy.linalg.hadamard(D).astype(np.float64) / math.sqrt(D)
+
+
+def _kv(rng, B, n, Hkv, scale=1.0):
+    """K and V as strided views of one interleaved buffer [B, n, (2 Hkv + 1) D]."""
+    buf = torch.from_numpy((rng.standard_normal((B, n, (2 * Hkv + 1) * D)) * scale).astype(np.float32))
+    buf = buf.to(torch.bfloat16)
+    k = buf[:, :, D:(Hkv + 1) * D].view(B, n, Hkv, D)
+    v = buf[:, :, (Hkv + 1) * D:].view(B, n, Hkv, D)
+    return buf, k, v
+
+
+def _cache_host(cache, T):
+    return (cache.k8[:, :, :T].cpu().numpy(), cache.k_scale[:, :, :T].cpu().numpy(),
+            cache.v[:, :, :T].cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+def test_append_matches_oracle_byte_for_byte():
+    import quantized_exact_order_amd as sage
+    rng = np.random.default_rng(20)
+    B, n, Hkv, t0, cap = 2, 300, 3, 17, 400
+    banner(f"kv_append B={B} n={n} Hkv={Hkv} t0={t0}")
+    buf, k, v = _kv(rng, B, n, Hkv, scale=3.0)
+    dbuf = buf.cuda()
+    dk = dbuf[:, :, D:(Hkv + 1) * D].view(B, n, Hkv, D)
+    dv = dbuf[:, :, (Hkv + 1) * D:].view(B, n, Hkv, D)
+    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
+    cache.k8.fill_(0x55)
+    sage.kv_append(cache, dk, dv, t0)
+    torch.cuda.synchronize()
+    k8, ks = oracle.kv_quant(k)
+    assert np.array_equal(cache.k8[:, :, t0:t0 + n].cpu().numpy(), k8)
+    assert np.array_equal(cache.k_scale[:, :, t0:t0 + n].cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert torch.equal(cache.v[:, :, t0:t0 + n].cpu().view(torch.int16), v.permute(0, 2, 1, 3).view(torch.int16))
+    assert (cache.k8[:, :, :t0] == 0x55).all() and (cache.k8[:, :, t0 + n:] == 0x55).all()
+
+
+def test_append_in_pieces_equals_one_append():
+    import quantized_exact_order_amd as sage
+    rng = np.random.default_rng(21)
+    B, n, Hkv = 1, 200, 2
+    banner("kv_append in pieces")
+    _, k, v = _kv(rng, B, n, Hkv)
+    k, v = k.cuda(), v.cuda()
+    a = sage.KvCache.allocate(B, Hkv, n, "cuda")
+    b = sage.KvCache.allocate(B, Hkv, n, "cuda")
+    sage.kv_append(a, k, v, 0)
+    for s, e in ((0, 1), (1, 64), (64, 130), (130, 200)):
+        sage.kv_append(b, k[:, s:e], v[:, s:e], s)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k8, b.k8) and torch.equal(a.k_scale.view(torch.int32), b.k_scale.view(torch.int32))
+    assert torch.equal(a.v.view(torch.int16), b.v.view(torch.int16))
+
+
+def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label=""):
+    import quantized_exact_order_amd as sage
+    rng = np.random.default_rng(seed)
+    banner(f"decode {label} B={B} Hq={Hq} Hkv={Hkv} T={T}")
+    _, k, v = _kv(rng, B, T, Hkv)
+    q = torch.from_numpy((rng.standard_normal((B, Hq, D)) * q_scale).astype(np.float32)).to(torch.bfloat16)
+    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
+    sage.kv_append(cache, k.cuda(), v.cuda(), 0)
+    o = sage.decode_attn(cache, q.cuda(), T)
+    torch.cuda.synchronize()
+    k8, ks, vc = _cache_host(cache, T)
+    o_ref, _ = oracle.decode_attn(q, k8, ks, vc, T)
+    g = o.cpu().float().numpy().astype(np.float64)
+    r = oracle.bf16_to_f32(o_ref).astype(np.float64)
+    err = np.abs(g - r)
+    print(f"[gpu] {label}: max-abs {err.max():.3g} (scale {np.abs(r).max():.3g}), "
+          f"differing {np.mean(g != r):.4f}, cos {oracle.cosine(g, r):.7f}", flush=True)
+    assert err.max() <= 2 ** -7 * np.abs(r).max()
+    assert oracle.cosine(g, r) >= 0.99999
+
+
+@pytest.mark.parametrize("Hq", [2, 4, 8, 16, 32])
+def test_decode_group_sizes(Hq):
+    _check_decode(2, Hq, 2, 300, 320, seed=30 + Hq, label=f"grp {Hq // 2}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 255, 256, 257, 511, 513, 1000])
+def test_decode_token_counts(T):
+    _check_decode(1, 8, 2, T, 1024, seed=40 + T, q_scale=2.0, label=f"T={T}")
+
+
+@pytest.mark.timeout(300)
+def test_decode_long_context():
+    _check_decode(1, 16, 4, 32768, 32768, seed=50, q_scale=2.0, label="32k tokens")
+
+
+@pytest.mark.parametrize("mult", [1, 8, 30])
+def test_kld_gate_on_gpu_cache(mult):
+    import quantized_exact_order_amd as sage
+    rng = np.random.default_rng(60 + mult)
+    banner(f"KLD gate, outlier x{mult}")
+    klds = []
+    for _ in range(8):
+        kk = rng.standard_normal((512, D))
+        if mult != 1:
+            kk[:, rng.choice(D, 8, replace=False)] *= mult
+        k = torch.from_numpy(kk.astype(np.float32)).to(torch.bfloat16).view(1, 512, 1, D)
+        q = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).to(torch.bfloat16)
+        cache = sage.KvCache.allocate(1, 1, 512, "cuda")
+        sage.kv_append(cache, k.cuda(), k.cuda(), 0)
+        torch.cuda.synchronize()
+        k8, ks, _ = _cache_host(cache, 512)
+        kd = k8[0, 0].astype(np.float64) * ks[0, 0, :, None].astype(np.float64)
+        qr = HM @ q.float().numpy().astype(np.float64)
+        s_q = kd @ qr / math.sqrt(D)
+        s_f = k[0, :, 0].float().numpy().astype(np.float64) @ q.float().numpy().astype(np.float64) / math.sqrt(D)
+        pq = np.exp(s_q - s_q.max()); pq /= pq.sum()
+        pf = np.exp(s_f - s_f.max()); pf /= pf.sum()
+        klds.append(float(np.sum(pf * (np.log(pf) - np.log(pq)))))
+    print(f"[gpu] outlier x{mult}: KLD {np.mean(klds):.3g}", flush=True)
+    assert np.mean(klds) <= 1e-3

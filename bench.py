@@ -20,6 +20,12 @@ seeded layers of N=729, H=16, D=128, each prep + quant + attention, run (a) as
 HIP graph and replayed, and (c) as one call with the layers stacked along the
 batch dimension (B = 27), which gives the attention launch 27x the
 work-groups of one layer.  All three must produce identical bytes.
+
+--workload decode times the decode-time INT8 K cache (per-head Hadamard
+rotation, one FP32 scale per (head, token), BF16 V): single-query attention
+of B=4 sequences x 32 query heads over 4 KV heads of D=256 and 32,768 cached
+tokens (HBM-bound: the cache is read once per step), and the append of a
+32,768-token prefill into the cache.
 """
 from __future__ import annotations
 
@@ -207,6 +213,63 @@ def run_encoder(args):
     print(json.dumps(result), flush=True)
 
 
+def run_decode(args):
+    """Decode step over the INT8 K cache and a prefill-sized append.  One JSON line."""
+    import torch
+    import quantized_exact_order_amd as sage
+
+    B, Hq, Hkv, D, T = 4, 32, 4, 256, 32768
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    print(f"[bench] decode cache B={B} Hq={Hq} Hkv={Hkv} D={D} T={T}", file=sys.stderr, flush=True)
+    kvbuf = torch.randn((B, T, 2 * Hkv * D), generator=g, device=dev).to(torch.bfloat16)
+    k = kvbuf[:, :, :Hkv * D].view(B, T, Hkv, D)
+    v = kvbuf[:, :, Hkv * D:].view(B, T, Hkv, D)
+    q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    cache = sage.KvCache.allocate(B, Hkv, T, dev)
+    ws = torch.empty(sage.decode_workspace(cache, Hq, T), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(args.steps, 1) * 10
+    t_append = timed(lambda: sage.kv_append(cache, k, v, 0), max(args.steps, 1))
+    t_decode = timed(lambda: sage.decode_attn(cache, q, T, o, ws), reps)
+    cache_bytes = B * Hkv * T * (D + 4 + 2 * D)            # k8 + k_scale + BF16 V, read once
+    step_bytes = cache_bytes + 2 * B * Hq * D * 2
+    append_bytes = B * T * Hkv * D * 2 * 2 + cache_bytes   # read K, V BF16; write the cache
+    gbps = step_bytes / (t_decode * 1e-3) / 1e9
+    result = {
+        "metric": "decode attention over the INT8 K cache: HBM GB/s (cache bytes / step time)",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": reps, "warmup": max(args.warmup, 1),
+        "ms_per_step": round(t_decode, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 K + bf16 V, fp32 math", "data": "synthetic",
+        "config": {"workload": "decode: B=4 sequences, 32 query heads over 4 KV heads, D=256, "
+                               "32,768 cached tokens, INT8 K (Hadamard-rotated, one scale per head and "
+                               "token) + BF16 V", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbps / 8000.0, 4), "bytes_per_step": step_bytes,
+                     "kernels": "decode_chunk_kernel<8> + decode_combine_kernel"},
+        "decode_steps_per_s": round(1e3 / t_decode, 1),
+        "append": {"tokens": B * T, "ms": round(t_append, 4),
+                   "GB_per_s": round(append_bytes / (t_append * 1e-3) / 1e9, 1)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,7 +278,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("canonical", "encoder"), default="canonical")
+    ap.add_argument("--workload", choices=("canonical", "encoder", "decode"), default="canonical")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
@@ -224,6 +287,8 @@ def main():
         sys.exit(2)
     if args.workload == "encoder":
         return run_encoder(args)
+    if args.workload == "decode":
+        return run_decode(args)
 
     import torch
     import workloads

@@ -208,7 +208,7 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
     if (st != SAGE_OK) return st;
     if (!bytes) return SAGE_E_NULL;
     if (Hq < 1 || T < 1 || T > cache->capacity) return SAGE_E_SHAPE;
-    *bytes = round256((size_t)cache->B * Hq * decode_chunks(T) * (cache->D + 2) * 4);
+    *bytes = round256((size_t)cache->B * Hq * decode_chunks(T) * sage::kPartStride * 4);
     return SAGE_OK;
 }
 

@@ -24,11 +24,14 @@ struct DecodeParams {
     const int8_t *k8;
     const float *k_scale;
     const uint16_t *vc;
-    float *part;                        // [B, Hq, nchunk, D + 2]: o partial, max, sum
+    float *part;                        // [B, Hq, nchunk, kPartStride]: o partial, max, sum
     uint16_t *o;                        // [B, Hq, D] BF16
 };
 
 constexpr int kDecodeChunk = 256;       // cached tokens per work-group
+// Chunk partial record: o[256], max, sum and two floats of padding, so that
+// every record starts 16-byte aligned.
+constexpr int kPartStride = 260;
 
 }  // namespace sage
 

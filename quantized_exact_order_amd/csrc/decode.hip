@@ -9,10 +9,11 @@
 // D = 256 (the page's head width; 1/sqrt(256) = 1/16 is exact).
 //
 // Decode reads the cache once: the work-group of (b, KV head, chunk of 256
-// tokens) serves all Hq/Hkv query heads of that KV head.  Lane t of a wave
-// scores token t of the wave's 64 (FP32 FMAs against the rotated queries,
-// broadcast from LDS); the chunk's softmax partial (max, sum, o) goes to a
-// workspace, and a second kernel combines the chunks in increasing order.
+// tokens) serves all Hq/Hkv query heads of that KV head.  Four lanes score one
+// token (a quarter of D each, FP32 FMAs against the rotated queries read from
+// LDS), so each K load instruction covers 16 rows in 64-byte runs; the
+// chunk's softmax partial (max, sum, o) goes to a workspace, and a second
+// kernel combines the chunks.
 
 #include "decode.h"
 
@@ -100,31 +101,54 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(const DecodeParams p)
     }
     __syncthreads();
 
-    // scores: lane <-> token
-    const int tl = wave * 64 + lane;                // token within the chunk
+    // scores: four lanes per token (lane = 4 tk + qd), lane qd taking the
+    // 16-byte pieces qd, qd + 4, ... of the row, 16 tokens of the wave per
+    // pass; the four partial sums meet by two lane exchanges and the scores go
+    // to pw (one entry per token)
+    const int tl = wave * 64 + lane;                // token within the chunk (softmax, PV)
     const int t = chunk * kDecodeChunk + tl;
     const bool valid = t < p.T;
-    float s[GRP];
+    {
+        const int tk = lane >> 2, qd = lane & 3;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int tc = wave * 64 + pass * 16 + tk;
+            const int tt = chunk * kDecodeChunk + tc;
+            float part[GRP];
 #pragma unroll
-    for (int g = 0; g < GRP; ++g) s[g] = 0.0f;
-    if (valid) {
-        const int8_t *kr = p.k8 + (cbase + t) * 256;
-        for (int d0 = 0; d0 < 256; d0 += 16) {
-            const int4 kk = *reinterpret_cast<const int4 *>(kr + d0);
-            const int w4[4] = {kk.x, kk.y, kk.z, kk.w};
-            float kf[16];
+            for (int g = 0; g < GRP; ++g) part[g] = 0.0f;
+            if (tt < p.T) {
+                const int8_t *kr = p.k8 + (cbase + tt) * 256 + 16 * qd;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) kf[i] = (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3)));
+                for (int d0 = 0; d0 < 256; d0 += 64) {        // the token's 4 lanes read 64 contiguous bytes
+                    const int4 kk = *reinterpret_cast<const int4 *>(kr + d0);
+                    const int w4[4] = {kk.x, kk.y, kk.z, kk.w};
+                    float kf[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) kf[i] = (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3)));
+#pragma unroll
+                    for (int g = 0; g < GRP; ++g) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) part[g] = __builtin_fmaf(qr[g][d0 + 16 * qd + i], kf[i], part[g]);
+                    }
+                }
+            }
 #pragma unroll
             for (int g = 0; g < GRP; ++g) {
+                part[g] = part[g] + shfl_xor_f(part[g], 1);
+                part[g] = part[g] + shfl_xor_f(part[g], 2);
+            }
+            if (qd == 0 && tt < p.T) {
+                const float sc = p.k_scale[cbase + tt] * 0.0625f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[g] = __builtin_fmaf(qr[g][d0 + i], kf[i], s[g]);
+                for (int g = 0; g < GRP; ++g) pw[g][tc] = part[g] * sc;
             }
         }
-        const float sc = p.k_scale[cbase + t] * 0.0625f;
-#pragma unroll
-        for (int g = 0; g < GRP; ++g) s[g] = s[g] * sc;
     }
+    __syncthreads();
+    float s[GRP];
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) s[g] = valid ? pw[g][tl] : 0.0f;
+    __syncthreads();
 
     // chunk softmax: maxima over the wave, then over the 4 waves
 #pragma unroll
@@ -149,38 +173,46 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(const DecodeParams p)
     }
     __syncthreads();
 
-    // PV over the wave's 64 tokens: lane <-> 4 dimensions
-    float o[GRP][4];
+    // PV over the wave's 64 tokens: lane = 32 hf + dl takes the tokens of
+    // parity hf and dimensions 8 dl .. 8 dl + 7 (16-byte V loads, two tokens
+    // per instruction); the two parities are added at the end
+    float o[GRP][8];
 #pragma unroll
     for (int g = 0; g < GRP; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[g][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) o[g][i] = 0.0f;
+    const int hf = lane >> 5, dl = lane & 31;
     const int tw = chunk * kDecodeChunk + wave * 64;
     const int nt = min(64, p.T - tw);
-    for (int j = 0; j < nt; ++j) {
-        float v[4];
-        load4(p.vc + (cbase + tw + j) * 256, lane, v);
+    for (int j = hf; j < nt; j += 2) {
+        const uint4 r = *reinterpret_cast<const uint4 *>(p.vc + (cbase + tw + j) * 256 + 8 * dl);
+        const float v[8] = {bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y),
+                            bf16_lo(r.z), bf16_hi(r.z), bf16_lo(r.w), bf16_hi(r.w)};
 #pragma unroll
         for (int g = 0; g < GRP; ++g) {
             const float e = pw[g][wave * 64 + j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[g][i] = __builtin_fmaf(e, v[i], o[g][i]);
+            for (int i = 0; i < 8; ++i) o[g][i] = __builtin_fmaf(e, v[i], o[g][i]);
         }
     }
+#pragma unroll
+    for (int g = 0; g < GRP; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[g][i] = o[g][i] + shfl_xor_f(o[g][i], 32);
     // waves in order 0..3
     for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
+        if (wave == w && hf == 0) {
 #pragma unroll
             for (int g = 0; g < GRP; ++g)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    osum[g][4 * lane + i] = (w == 0) ? o[g][i] : osum[g][4 * lane + i] + o[g][i];
+                for (int i = 0; i < 8; ++i)
+                    osum[g][8 * dl + i] = (w == 0) ? o[g][i] : osum[g][8 * dl + i] + o[g][i];
         }
         __syncthreads();
     }
     for (int g = wave; g < GRP; g += 4) {
         const int h = hk * GRP + g;
-        float *dst = p.part + (((int64_t)b * p.Hq + h) * p.nchunk + chunk) * (256 + 2);
+        float *dst = p.part + (((int64_t)b * p.Hq + h) * p.nchunk + chunk) * kPartStride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[4 * lane + i] = osum[g][4 * lane + i];
         if (lane == 0) {
@@ -190,25 +222,48 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(const DecodeParams p)
     }
 }
 
-// Combines the chunk partials of one query head in increasing chunk order:
-// M = max m_c, L = sum l_c e^(m_c - M), O = (sum o_c e^(m_c - M)) / L.
-// Grid (Hq, B), one wave.
-__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p) {
-    const int lane = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
-    const float *src = p.part + ((int64_t)b * p.Hq + h) * p.nchunk * (256 + 2);
+// Combines the chunk partials of one query head: M = max m_c,
+// L = sum l_c e^(m_c - M), O = (sum o_c e^(m_c - M)) / L.  Wave w sums the
+// chunks c = w, w + 4, ... in increasing order; the four wave sums are added
+// in the order 0, 1, 2, 3 (a fixed order: the result is deterministic).
+// Grid (Hq, B), 256 threads.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams p) {
+    __shared__ float wm[4];
+    __shared__ float wl[4];
+    __shared__ float wo[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = blockIdx.x, b = blockIdx.y;
+    const float *src = p.part + ((int64_t)b * p.Hq + h) * p.nchunk * kPartStride;
     float M = -INFINITY;
-    for (int c = 0; c < p.nchunk; ++c) M = __builtin_fmaxf(M, src[c * (256 + 2) + 256]);
+    for (int c = threadIdx.x; c < p.nchunk; c += 256) M = __builtin_fmaxf(M, src[c * kPartStride + 256]);
+    M = wave_max_f(M);
+    if (lane == 0) wm[wave] = M;
+    __syncthreads();
+    M = __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3]));
     float L = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < p.nchunk; ++c) {
-        const float *pc = src + c * (256 + 2);
+    for (int c = wave; c < p.nchunk; c += 4) {
+        const float *pc = src + c * kPartStride;
+        const float4 x = *reinterpret_cast<const float4 *>(pc + 4 * lane);
         const float f = expf(pc[256] - M);
         L = __builtin_fmaf(pc[257], f, L);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(pc[4 * lane + i], f, o[i]);
+        o[0] = __builtin_fmaf(x.x, f, o[0]);
+        o[1] = __builtin_fmaf(x.y, f, o[1]);
+        o[2] = __builtin_fmaf(x.z, f, o[2]);
+        o[3] = __builtin_fmaf(x.w, f, o[3]);
     }
-    const float r = 1.0f / L;
-    uint16_t *dst = p.o + ((int64_t)b * p.Hq + h) * 256 + 4 * lane;
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(o[0] * r, o[1] * r), pack_bf16x2(o[2] * r, o[3] * r));
+    if (lane == 0) wl[wave] = L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wo[wave][4 * lane + i] = o[i];
+    __syncthreads();
+    if (wave == 0) {
+        const float Lt = ((wl[0] + wl[1]) + wl[2]) + wl[3];
+        const float r = 1.0f / Lt;
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            t[i] = (((wo[0][4 * lane + i] + wo[1][4 * lane + i]) + wo[2][4 * lane + i]) + wo[3][4 * lane + i]) * r;
+        uint16_t *dst = p.o + ((int64_t)b * p.Hq + h) * 256 + 4 * lane;
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]));
+    }
 }
 
 }  // namespace
@@ -232,6 +287,6 @@ hipError_t sage_launch_decode(const sage::DecodeParams &p, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sage::decode_combine_kernel<<<dim3(p.Hq, p.B), 64, 0, s>>>(p);
+    sage::decode_combine_kernel<<<dim3(p.Hq, p.B), 256, 0, s>>>(p);
     return hipGetLastError();
 }

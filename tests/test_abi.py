@@ -147,7 +147,7 @@ def test_decode_cache_refusals_happen_before_launch(sage):
     assert append(cache(), 0, 1, SageView(A, 0, 512, 256, 2)) == "SAGE_E_STRIDE"
     n = ctypes.c_size_t()
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 64, ctypes.byref(n))) == "SAGE_OK"
-    assert n.value == 1 * 8 * 1 * 258 * 4 + (-(1 * 8 * 258 * 4) % 256)
+    assert n.value == 1 * 8 * 1 * 260 * 4 + (-(1 * 8 * 260 * 4) % 256)
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 65, ctypes.byref(n))) == "SAGE_E_SHAPE"
     q = SageView(A, 0, 8 * 256, 256, 1)
     attn = lambda c, Hq, T, ws=A, wsb=1 << 30, o=A: name(lib.sage_decode_attn(

@@ -27,15 +27,28 @@ _BUILD = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD, "libsage_oracle.so")
 _lib = None
 
+# gcc flags of the oracle library: strict IEEE binary32, no contraction.
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+             "-Wall", "-Wextra", "-Wno-unused-parameter", "-fPIC", "-shared"]
+
+# Mutation testing of the pins: when set, this names an already compiled
+# variant of sage_oracle.c that is loaded instead of the in-tree build.
+_OVERRIDE = os.environ.get("SAGE_ORACLE_LIB_OVERRIDE")
+
+
+def compile_source(src: str, out: str) -> None:
+    """gcc ``src`` into the shared library ``out`` with the oracle's flags."""
+    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", out, "-lm"], check=True)
+
 
 def build(force: bool = False) -> str:
     """Compile the oracle shared library with gcc (no GPU toolchain involved)."""
+    if _OVERRIDE:
+        return _OVERRIDE
     os.makedirs(_BUILD, exist_ok=True)
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
-               "-Wall", "-Wextra", "-Wno-unused-parameter", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
+        compile_source(_SRC, tmp)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -43,8 +56,7 @@ def build(force: bool = False) -> str:
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(build())
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]

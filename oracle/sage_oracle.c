@@ -513,7 +513,6 @@ void oracle_attn_rows_mode(int B, int N, int Hq, int Hkv, int D,
     }
 }
 
-/* Number of OpenMP threads the oracle runs with (for reporting). */
 /* The FP32 per-tile partial (pv_fp16 = 0) is the oracle's reading and the
  * parity target; pv_fp16 = 1 emulates the page's two-level PV (each 64-key
  * partial accumulated in FP16 by two ordered K=32 steps, then added to the
@@ -620,6 +619,7 @@ void oracle_decode_attn(int B, int Hq, int Hkv, int D, int T, int Tc, const uint
         }
 }
 
+/* Number of OpenMP threads the oracle runs with (for reporting). */
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

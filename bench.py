@@ -256,13 +256,13 @@ def run_decode(args):
         "n_gpus": 1, "steps": reps, "warmup": max(args.warmup, 1),
         "ms_per_step": round(t_decode, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8 K + bf16 V, fp32 math", "data": "synthetic",
+        "dtype": "int8 K (i8 MFMA) + bf16 V (bf16 MFMA), fp32 accumulation", "data": "synthetic",
         "config": {"workload": "decode: B=4 sequences, 32 query heads over 4 KV heads, D=256, "
                                "32,768 cached tokens, INT8 K (Hadamard-rotated, one scale per head and "
                                "token) + BF16 V", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(gbps / 8000.0, 4), "bytes_per_step": step_bytes,
-                     "kernels": "decode_chunk_kernel<8> + decode_combine_kernel"},
+                     "kernels": "decode_chunk_kernel + decode_combine_kernel"},
         "decode_steps_per_s": round(1e3 / t_decode, 1),
         "append": {"tokens": B * T, "ms": round(t_append, 4),
                    "GB_per_s": round(append_bytes / (t_append * 1e-3) / 1e9, 1)},

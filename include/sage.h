@@ -156,10 +156,13 @@ sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *
  * orthogonal.  V is kept in BF16.  Head width D = 256 only.
  * ------------------------------------------------------------------------ */
 
-/* The cache, owned by the caller (device memory, 16-byte aligned):
- *   k8       INT8 [B, Hkv, capacity, D]  rotated K rows
- *   k_scale  FP32 [B, Hkv, capacity]     amax / 127 of each rotated row
- *   v        BF16 [B, Hkv, capacity, D]  V rows                             */
+/* The cache, owned by the caller (device memory, 16-byte aligned, capacity a
+ * multiple of 8):
+ *   k8       INT8 [B, Hkv, capacity, D]          rotated K rows
+ *   k_scale  FP32 [B, Hkv, capacity]             amax / 127 of each rotated row
+ *   v        BF16 [B, Hkv, capacity / 8, D, 8]   V in blocks of 8 tokens per
+ *            channel: token t, channel d of a (batch, KV head) at
+ *            ((t / 8) * D + d) * 8 + t % 8                                   */
 typedef struct sage_kv_cache {
     int8_t *k8;
     float *k_scale;
@@ -170,9 +173,12 @@ typedef struct sage_kv_cache {
 /* Writes n new tokens at cache positions [t0, t0 + n): per row (b, t, h) of
  * the BF16 views k and v ([B, n, Hkv, D], unit d stride, 16-byte aligned
  * rows), u = H k / 16, k_scale = max(1e-7, max|u|) / 127,
- * k8 = round-half-even-saturate(u * (127 / max(1e-7, max|u|))), v copied.
+ * k8 = round-half-even-saturate(u * (127 / max(1e-7, max|u|))), v copied
+ * into its blocks (the other tokens of a partly written block keep their
+ * values).
  * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256), SAGE_E_SHAPE
- * (B, Hkv, n < 1, t0 < 0 or t0 + n > capacity), SAGE_E_STRIDE,
+ * (B, Hkv, capacity not a multiple of 8, n < 1, t0 < 0 or
+ * t0 + n > capacity), SAGE_E_STRIDE,
  * SAGE_E_ALIGN, SAGE_E_HIP. */
 sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, const sage_view_bf16 *v,
                            int32_t t0, int32_t n, void *stream);
@@ -183,12 +189,15 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
 /* Single-query attention of each of the Hq query heads (view q [B, 1, Hq, D])
  * over cache positions [0, T) of KV head h / (Hq / Hkv):
  *   s_t = ((H q / 16) . k8_t) * k_scale_t / 16,  w = softmax(s),
- *   o = bf16(sum_t w_t v_t)                     (FP32 on the GPU)
+ *   o = bf16(sum_t w_t v_t)
  * o: BF16 [B, Hq, D] contiguous.  The cache is read once: the work-group of
- * one KV head and 256 tokens serves its Hq / Hkv query heads, and the chunk
- * partials are combined in increasing token order (deterministic).
- * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256, Hq / Hkv not 1, 2,
- * 4, 8 or 16), SAGE_E_GQA, SAGE_E_SHAPE (T < 1 or T > capacity),
+ * one KV head and 256 tokens serves its Hq / Hkv query heads on the matrix
+ * cores (exact INT32 dot products of K with a three-part INT8 expansion of
+ * the rotated query; BF16 V times a two-part BF16 split of the weights, FP32
+ * accumulation), and the chunk partials are combined in a fixed order
+ * (deterministic).
+ * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256, Hq / Hkv > 16),
+ * SAGE_E_GQA, SAGE_E_SHAPE (T < 1 or T > capacity),
  * SAGE_E_STRIDE, SAGE_E_ALIGN, SAGE_E_WORKSPACE, SAGE_E_HIP. */
 sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
                              void *o, void *workspace, size_t ws_bytes, void *stream);

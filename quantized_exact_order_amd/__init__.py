@@ -169,13 +169,21 @@ class KvCache:
     """Device tensors behind sage_kv_cache (D = 256)."""
     k8: torch.Tensor         # int8  [B, Hkv, capacity, D], rotated K rows
     k_scale: torch.Tensor    # f32   [B, Hkv, capacity]
-    v: torch.Tensor          # bf16  [B, Hkv, capacity, D]
+    v: torch.Tensor          # bf16  [B, Hkv, capacity / 8, D, 8], blocks of 8 tokens per channel
 
     @classmethod
     def allocate(cls, B: int, Hkv: int, capacity: int, device, D: int = 256) -> "KvCache":
+        """Zeroed cache; capacity must be a multiple of 8."""
+        if capacity % 8:
+            raise ValueError("capacity must be a multiple of 8")
         return cls(torch.zeros((B, Hkv, capacity, D), dtype=torch.int8, device=device),
                    torch.zeros((B, Hkv, capacity), dtype=torch.float32, device=device),
-                   torch.zeros((B, Hkv, capacity, D), dtype=torch.bfloat16, device=device))
+                   torch.zeros((B, Hkv, capacity // 8, D, 8), dtype=torch.bfloat16, device=device))
+
+    def v_rows(self) -> torch.Tensor:
+        """The cached V as BF16 [B, Hkv, capacity, D] (a copy)."""
+        B, Hkv, nb, D, _ = self.v.shape
+        return self.v.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nb * 8, D)
 
     def c(self) -> SageKvCache:
         B, Hkv, cap, D = self.k8.shape

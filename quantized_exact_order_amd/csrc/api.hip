@@ -169,6 +169,7 @@ sage_status check_cache(const sage_kv_cache *c) {
     if (!c || !c->k8 || !c->k_scale || !c->v) return SAGE_E_NULL;
     if (c->D != 256) return SAGE_E_UNSUPPORTED;
     if (c->B < 1 || c->B > 65535 || c->Hkv < 1 || c->capacity < 1) return SAGE_E_SHAPE;
+    if (c->capacity % sage::kVBlock != 0) return SAGE_E_SHAPE;
     if ((int64_t)c->B * c->Hkv * c->capacity > (int64_t(1) << 34)) return SAGE_E_SHAPE;
     if (!aligned16(c->k8) || !aligned16(c->k_scale) || !aligned16(c->v)) return SAGE_E_ALIGN;
     return SAGE_OK;
@@ -182,7 +183,6 @@ sage_status check_view_any(const sage_view_bf16 *v) {
     return SAGE_OK;
 }
 
-int64_t decode_chunks(int32_t T) { return (T + sage::kDecodeChunk - 1) / sage::kDecodeChunk; }
 
 }  // namespace
 
@@ -193,10 +193,12 @@ sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, 
     if ((st = check_view_any(k)) != SAGE_OK) return st;
     if ((st = check_view_any(v)) != SAGE_OK) return st;
     if (n < 1 || t0 < 0 || (int64_t)t0 + n > cache->capacity) return SAGE_E_SHAPE;
-    if ((int64_t)n * cache->Hkv > 2147483647LL - 3) return SAGE_E_SHAPE;
+    const int64_t nblk = ((int64_t)t0 + n - 1) / sage::kVBlock - t0 / sage::kVBlock + 1;
+    if (nblk * cache->Hkv > 2147483647LL - 3) return SAGE_E_SHAPE;
     sage::KvAppendParams p;
     std::memset(&p, 0, sizeof(p));
     p.B = cache->B; p.Hkv = cache->Hkv; p.D = cache->D; p.n = n; p.t0 = t0; p.cap = cache->capacity;
+    p.nblk = (int)nblk;
     p.k = sage::View{static_cast<const uint16_t *>(k->ptr), k->sb, k->sn, k->sh};
     p.v = sage::View{static_cast<const uint16_t *>(v->ptr), v->sb, v->sn, v->sh};
     p.k8 = cache->k8; p.k_scale = cache->k_scale; p.vc = cache->v;
@@ -208,7 +210,7 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
     if (st != SAGE_OK) return st;
     if (!bytes) return SAGE_E_NULL;
     if (Hq < 1 || T < 1 || T > cache->capacity) return SAGE_E_SHAPE;
-    *bytes = round256((size_t)cache->B * Hq * decode_chunks(T) * sage::kPartStride * 4);
+    *bytes = round256((size_t)sage::decode_ws_bytes(cache->B, Hq, cache->Hkv, T));
     return SAGE_OK;
 }
 
@@ -222,16 +224,19 @@ sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_
     if (Hq < 1 || T < 1 || T > cache->capacity) return SAGE_E_SHAPE;
     if (Hq % cache->Hkv != 0) return SAGE_E_GQA;
     const int grp = Hq / cache->Hkv;
-    if (grp != 1 && grp != 2 && grp != 4 && grp != 8 && grp != 16) return SAGE_E_UNSUPPORTED;
+    if (grp > sage::kDecodeMaxGroup) return SAGE_E_UNSUPPORTED;
     size_t need = 0;
     if ((st = sage_decode_workspace(cache, Hq, T, &need)) != SAGE_OK) return st;
     if (!workspace || ws_bytes < need) return SAGE_E_WORKSPACE;
     if (!aligned16(workspace)) return SAGE_E_ALIGN;
-    if (decode_chunks(T) * cache->Hkv > 2147483647LL) return SAGE_E_SHAPE;
+    const int64_t nchunk = sage::decode_nchunk(cache->B, cache->Hkv, T);
+    if (nchunk * cache->Hkv > 2147483647LL) return SAGE_E_SHAPE;
     sage::DecodeParams p;
     std::memset(&p, 0, sizeof(p));
     p.B = cache->B; p.Hq = Hq; p.Hkv = cache->Hkv; p.grp = grp; p.D = cache->D; p.T = T;
-    p.cap = cache->capacity; p.nchunk = (int)decode_chunks(T);
+    p.cap = cache->capacity;
+    p.ns = sage::decode_steps(cache->B, cache->Hkv, T);
+    p.nchunk = (int)nchunk;
     p.q = sage::View{static_cast<const uint16_t *>(q->ptr), q->sb, q->sn, q->sh};
     p.k8 = cache->k8; p.k_scale = cache->k_scale; p.vc = cache->v;
     p.part = static_cast<float *>(workspace);

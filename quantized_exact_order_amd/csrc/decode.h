@@ -6,20 +6,26 @@
 
 namespace sage {
 
+// V cache layout: BF16 blocks of 8 consecutive tokens per channel, element
+// (t, d) of a (batch, KV head) at ((t / 8) * D + d) * 8 + t % 8, so that one
+// 16-byte load gives a channel's 8 tokens (the B operand of the PV MFMA).
+constexpr int kVBlock = 8;
+
 // Appends n rows to the cache at positions [t0, t0 + n): K rotated by the
 // normalized Walsh-Hadamard transform and quantized to INT8 with one FP32
-// scale per (head, token); V copied as BF16.
+// scale per (head, token); V copied as BF16 into its 8-token blocks.
 struct KvAppendParams {
-    int B, Hkv, D, n, t0, cap;
+    int B, Hkv, D, n, t0, cap, nblk;    // nblk: 8-token blocks touched by [t0, t0 + n)
     View k, v;                          // [B, n, Hkv, D] BF16 views
     int8_t *k8;                         // [B, Hkv, cap, D]
     float *k_scale;                     // [B, Hkv, cap]
-    uint16_t *vc;                       // [B, Hkv, cap, D]
+    uint16_t *vc;                       // [B, Hkv, cap / 8, D, 8]
 };
 
 // Single-query attention of each query head over the first T cached tokens.
 struct DecodeParams {
-    int B, Hq, Hkv, grp, D, T, cap, nchunk;
+    int B, Hq, Hkv, grp, D, T, cap;
+    int ns, nchunk;                     // 32-token steps per wave; chunks of 128 * ns tokens
     View q;                             // [B, 1, Hq, D] BF16 view (n = 0)
     const int8_t *k8;
     const float *k_scale;
@@ -28,10 +34,26 @@ struct DecodeParams {
     uint16_t *o;                        // [B, Hq, D] BF16
 };
 
-constexpr int kDecodeChunk = 256;       // cached tokens per work-group
+constexpr int kDecodeMaxGroup = 16;     // query heads per KV head (MFMA columns)
+constexpr int kDecodeMaxSteps = 16;
 // Chunk partial record: o[256], max, sum and two floats of padding, so that
 // every record starts 16-byte aligned.
 constexpr int kPartStride = 260;
+
+// Steps per wave: about 512 work-groups over the whole cache (two per CU),
+// between 1 and kDecodeMaxSteps.
+inline int decode_steps(int B, int Hkv, int T) {
+    const int64_t ns = (int64_t)B * Hkv * T / (128 * 512);
+    return ns < 1 ? 1 : (ns > kDecodeMaxSteps ? kDecodeMaxSteps : (int)ns);
+}
+inline int64_t decode_nchunk(int B, int Hkv, int T) {
+    const int64_t c = 128 * (int64_t)decode_steps(B, Hkv, T);
+    return (T + c - 1) / c;
+}
+// Workspace: the chunk partials.
+inline int64_t decode_ws_bytes(int B, int Hq, int Hkv, int T) {
+    return (int64_t)B * Hq * decode_nchunk(B, Hkv, T) * kPartStride * 4;
+}
 
 }  // namespace sage
 

@@ -8,12 +8,22 @@
 //           o = sum_t w_t v_t, rounded to BF16.
 // D = 256 (the page's head width; 1/sqrt(256) = 1/16 is exact).
 //
-// Decode reads the cache once: the work-group of (b, KV head, chunk of 256
-// tokens) serves all Hq/Hkv query heads of that KV head.  Four lanes score one
-// token (a quarter of D each, FP32 FMAs against the rotated queries read from
-// LDS), so each K load instruction covers 16 rows in 64-byte runs; the
-// chunk's softmax partial (max, sum, o) goes to a workspace, and a second
-// kernel combines the chunks.
+// Decode reads the cache once: the work-group of (b, KV head, chunk of
+// 128 ns tokens) serves all Hq/Hkv (<= 16) query heads of that KV head, each
+// wave streaming its 32 ns tokens in steps of 32 with an online softmax, and
+// both contractions run on the matrix cores:
+//   * scores: the rotated query of each head is expanded as
+//     qr = s1 q1 + s2 q2 + s3 q3 + r with INT8 parts q_j, s_{j+1} = s_j / 128
+//     and |r| <= s3 / 2 (below FP32 rounding of qr . k8), so that
+//     qr . k8 = sum_j s_j (q_j . k8) with exact INT32 dot products
+//     (v_mfma_i32_16x16x64_i8: 16 tokens x 16 heads, K rows read straight
+//     from the cache as the A operand);
+//   * PV: w = w_hi + w_lo (two BF16 parts, |w_lo| <= 2^-9 |w|, the rest below
+//     2^-17 |w|) times BF16 V (v_mfma_f32_16x16x32_bf16, FP32 accumulation);
+//     the cache keeps V in 8-token blocks per channel, so one 16-byte load is
+//     a lane's B operand.
+// The chunk's softmax partial (max, sum, o) goes to a workspace, and a second
+// kernel combines the chunks in a fixed order.
 
 #include "decode.h"
 
@@ -51,17 +61,14 @@ __device__ __forceinline__ void load4(const uint16_t *row, int lane, float x[4])
     x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
 }
 
-// One wave per appended row (b, t, h): 4 rows per 256-thread block.
-// Grid (ceil(n * Hkv / 4), B).
-__global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= p.n * p.Hkv) return;
-    const int t = row / p.Hkv, h = row % p.Hkv, b = blockIdx.y;
-    const int64_t c = ((int64_t)b * p.Hkv + h) * p.cap + p.t0 + t;     // cache row
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
+// Rotates, quantizes and stores K row t (cache position) of head h; one wave.
+__device__ __forceinline__ void append_k_row(const KvAppendParams &p, int b, int h, int t, int lane) {
+    const int64_t c = ((int64_t)b * p.Hkv + h) * p.cap + t;          // cache row
     float u[4];
-    load4(p.k.ptr + (int64_t)b * p.k.sb + (int64_t)t * p.k.sn + (int64_t)h * p.k.sh, lane, u);
+    load4(p.k.ptr + (int64_t)b * p.k.sb + (int64_t)(t - p.t0) * p.k.sn + (int64_t)h * p.k.sh, lane, u);
     wht256(u, lane);
     float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
                               __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
@@ -73,196 +80,388 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) 
     for (int i = 0; i < 4; ++i) w |= (uint32_t)(to_i8(u[i] * mul) & 0xff) << (8 * i);
     reinterpret_cast<uint32_t *>(p.k8 + c * 256)[lane] = w;
     if (lane == 0) p.k_scale[c] = amax / 127.0f;
-
-    const uint2 v = *reinterpret_cast<const uint2 *>(p.v.ptr + (int64_t)b * p.v.sb + (int64_t)t * p.v.sn +
-                                                    (int64_t)h * p.v.sh + 4 * lane);
-    reinterpret_cast<uint2 *>(p.vc + c * 256)[lane] = v;
 }
 
-// Chunk partial of GRP query heads.  Grid (nchunk * Hkv, B), 256 threads.
-template <int GRP>
-__global__ __launch_bounds__(256) void decode_chunk_kernel(const DecodeParams p) {
-    __shared__ float qr[GRP][256];                 // rotated queries
-    __shared__ float pw[GRP][kDecodeChunk];        // exp(s - chunk max)
-    __shared__ float red[4][GRP];                  // per-wave maxima, then sums
-    __shared__ float osum[GRP][256];
+// One wave per (b, KV head, 8-token block touched by [t0, t0 + n)): the K rows
+// of the block's new tokens one by one, then the V block, lane owning
+// channels 4 lane .. 4 lane + 3 (four 16-byte vectors of 8 tokens each; the
+// tokens of the block outside [t0, t0 + n) keep their cached values).
+// Grid (ceil(nblk * Hkv / 4), B).
+__global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= p.nblk * p.Hkv) return;
+    const int h = item % p.Hkv, blk = (p.t0 >> 3) + item / p.Hkv, b = blockIdx.y;
+    const int tb = kVBlock * blk;
+    const int ta = max(tb, p.t0), te = min(tb + kVBlock, p.t0 + p.n);    // new tokens [ta, te)
+    for (int t = ta; t < te; ++t) append_k_row(p, b, h, t, lane);
+
+    uint4 *dst = reinterpret_cast<uint4 *>(
+        p.vc + ((((int64_t)b * p.Hkv + h) * (p.cap / kVBlock) + blk) * 256 + 4 * lane) * kVBlock);
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 old = make_uint4(0, 0, 0, 0);
+        if (te - ta < kVBlock) old = dst[i];
+        w[i][0] = old.x; w[i][1] = old.y; w[i][2] = old.z; w[i][3] = old.w;
+    }
+#pragma unroll
+    for (int e = 0; e < kVBlock; ++e) {
+        const int t = tb + e;
+        if (t >= ta && t < te) {
+            const uint2 s = *reinterpret_cast<const uint2 *>(p.v.ptr + (int64_t)b * p.v.sb +
+                                                             (int64_t)(t - p.t0) * p.v.sn +
+                                                             (int64_t)h * p.v.sh + 4 * lane);
+            const uint32_t hv[4] = {s.x & 0xffffu, s.x >> 16, s.y & 0xffffu, s.y >> 16};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t &x = w[i][e >> 1];
+                x = (e & 1) ? ((x & 0x0000ffffu) | (hv[i] << 16)) : ((x & 0xffff0000u) | hv[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+}
+
+constexpr int kQRow = 272;      // LDS bytes per head row of the query parts (rows 4 banks apart)
+
+// The A operands (K rows) and K scales of the 32-token step starting at ts:
+// MFMA block bb row m is token ts + 8 (m / 4) + 4 bb + m % 4 (clamped to the
+// last valid row), so that accumulator register i of lane group q4 is token
+// ts + 8 q4 + 4 bb + i; k0, k1 get the scales of tokens ts + 8 q4 .. + 7.
+struct KStep {
+    v4i a[2][4];
+    float4 k0, k1;
+};
+
+__device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const float *ksb, int ts, int T,
+                                            int q4, int r16) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const int tok = min(ts + 8 * (r16 >> 2) + 4 * bb + (r16 & 3), T - 1);
+        const int8_t *kr = kb + (int64_t)tok * 256 + 16 * q4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) k.a[bb][s] = *reinterpret_cast<const v4i *>(kr + 64 * s);
+    }
+    // a group of 8 past T reads the last valid group (its scores are masked);
+    // t8 + 8 <= capacity since both are multiples of 8
+    const int t8 = min(ts + 8 * q4, ((T - 1) / 8) * 8);
+    k.k0 = *reinterpret_cast<const float4 *>(ksb + t8);
+    k.k1 = *reinterpret_cast<const float4 *>(ksb + t8 + 4);
+}
+
+// The V block of tokens ts + 8 q4 .. + 7 for channels 16 nb + r16 (the B
+// operands of the step); a block past T reads the last valid block and is
+// masked to zero before use.
+__device__ __forceinline__ void load_v_step(uint4 vv[16], const uint16_t *vb, int ts, int T, int q4, int r16) {
+    const int blk = min(ts / kVBlock + q4, (T - 1) / kVBlock);
+    const uint16_t *vr = vb + ((int64_t)blk * 256 + r16) * kVBlock;
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) vv[nb] = *reinterpret_cast<const uint4 *>(vr + nb * 16 * kVBlock);
+}
+
+// Chunk partial of the grp (<= 16) query heads of one KV head over tokens
+// [128 ns chunk, 128 ns (chunk + 1)).  Grid (nchunk * Hkv, B), 256 threads;
+// wave w streams tokens 128 ns chunk + 32 ns w + [0, 32 ns) in steps of 32
+// with an online softmax (each step's V loads are issued before its K loads,
+// so they are in flight while the scores compute), and the four waves'
+// partials are merged in order.  The query expansion runs while the first
+// step's loads are in flight.
+__global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams p) {
+    __shared__ __attribute__((aligned(16))) int8_t qp[3][kDecodeMaxGroup][kQRow];   // query parts
+    __shared__ float qsc[3][kDecodeMaxGroup];                                        // their scales
+    __shared__ float wm[4][kDecodeMaxGroup];                                         // per-wave maxima
+    __shared__ float wl[4][kDecodeMaxGroup];                                         // per-wave sums
+    __shared__ __attribute__((aligned(16))) float osum[kDecodeMaxGroup][260];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q4 = lane >> 4, r16 = lane & 15;
     const int hk = blockIdx.x % p.Hkv, chunk = blockIdx.x / p.Hkv, b = blockIdx.y;
-    const int64_t cbase = ((int64_t)b * p.Hkv + hk) * p.cap;
+    const int64_t bh = (int64_t)b * p.Hkv + hk;
+    const int T = p.T;
 
-    for (int g = wave; g < GRP; g += 4) {
-        float x[4];
-        const int h = hk * GRP + g;
-        load4(p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh, lane, x);
-        wht256(x, lane);
+    const int tw = (chunk * 4 + wave) * 32 * p.ns;
+    const int nst = T > tw ? min((T - tw + 31) / 32, p.ns) : 0;
+    const int8_t *kb = p.k8 + bh * p.cap * 256;
+    const float *ksb = p.k_scale + bh * p.cap;
+    const uint16_t *vb = p.vc + bh * p.cap * 256;
+    // the query rows of this wave's heads g = wave + 4 i are loaded first, so
+    // that waiting for them does not wait for the step loads issued after
+    // (unconditionally: heads g >= grp read head grp - 1, are expanded like
+    // the others and then zeroed, so no load is sunk into a conditional block
+    // whose wait would also wait for the step loads)
+    float xq[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qr[g][4 * lane + i] = x[i];
+    for (int i = 0; i < 4; ++i) {
+        const int g = min(wave + 4 * i, p.grp - 1);
+        load4(p.q.ptr + (int64_t)b * p.q.sb + (int64_t)(hk * p.grp + g) * p.q.sh, lane, xq[i]);
+    }
+    // the first step's loads, unconditionally (a wave with no tokens reads
+    // clamped, valid rows and does not use them)
+    KStep k;
+    uint4 vv[16];
+    load_v_step(vv, vb, tw, T, q4, r16);
+    load_k_step(k, kb, ksb, tw, T, q4, r16);
+    __builtin_amdgcn_sched_barrier(0);      // every load above is issued before the expansion
+
+    // rotated queries -> three INT8 parts q_j with scales s_j (s_{j+1} =
+    // s_j / 128), qr = sum_j s_j q_j + r, |r| <= s3 / 2; zero rows for the
+    // unused MFMA columns g >= grp
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = wave + 4 * i;
+        uint32_t wd[3] = {0u, 0u, 0u};
+        float sj[3] = {0.0f, 0.0f, 0.0f};
+        float *x = xq[i];
+        wht256(x, lane);
+        float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                                  __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
+        a = wave_max_f(a);
+        float sc = a / 127.0f, mu = 127.0f / a;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const bool ok = a > 0.0f && mu <= 3.0e38f;      // a nonzero row, a finite multiplier
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qv = ok ? to_i8(x[e] * mu) : 0;
+                wd[j] |= (uint32_t)(qv & 0xff) << (8 * e);
+                x[e] = __builtin_fmaf(-(float)qv, sc, x[e]);
+            }
+            sj[j] = a > 0.0f ? sc : 0.0f;
+            sc = sc * 0.0078125f;
+            mu = mu * 128.0f;
+        }
+        const bool used = g < p.grp;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            *reinterpret_cast<uint32_t *>(&qp[j][g][4 * lane]) = used ? wd[j] : 0u;
+            if (lane == 0) qsc[j][g] = used ? sj[j] : 0.0f;
+        }
     }
     __syncthreads();
+    const float s1 = qsc[0][r16], s2 = qsc[1][r16], s3 = qsc[2][r16];
 
-    // scores: four lanes per token (lane = 4 tk + qd), lane qd taking the
-    // 16-byte pieces qd, qd + 4, ... of the row, 16 tokens of the wave per
-    // pass; the four partial sums meet by two lane exchanges and the scores go
-    // to pw (one entry per token)
-    const int tl = wave * 64 + lane;                // token within the chunk (softmax, PV)
-    const int t = chunk * kDecodeChunk + tl;
-    const bool valid = t < p.T;
-    {
-        const int tk = lane >> 2, qd = lane & 3;
-        for (int pass = 0; pass < 4; ++pass) {
-            const int tc = wave * 64 + pass * 16 + tk;
-            const int tt = chunk * kDecodeChunk + tc;
-            float part[GRP];
+    float m = -INFINITY, l = 0.0f;          // running max and lane-partial sum of head r16
+    v4f o[16];                              // register i: head 4 q4 + i, channel 16 nb + r16
 #pragma unroll
-            for (int g = 0; g < GRP; ++g) part[g] = 0.0f;
-            if (tt < p.T) {
-                const int8_t *kr = p.k8 + (cbase + tt) * 256 + 16 * qd;
+    for (int nb = 0; nb < 16; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int st = 0; st < nst; ++st) {
+        const int ts = tw + 32 * st;
+        if (st > 0) {
+            load_v_step(vv, vb, ts, T, q4, r16);
+            load_k_step(k, kb, ksb, ts, T, q4, r16);
+        }
+
+        // scores of tokens ts + 8 q4 + e, head r16: B operand (part j, d-step
+        // s) = bytes 16 q4 + 64 s .. + 15 of part j of head r16
+        float sc[8];
+        const int t8 = ts + 8 * q4;
+        const float ks[8] = {k.k0.x, k.k0.y, k.k0.z, k.k0.w, k.k1.x, k.k1.y, k.k1.z, k.k1.w};
+        v4i acc[2][3];
 #pragma unroll
-                for (int d0 = 0; d0 < 256; d0 += 64) {        // the token's 4 lanes read 64 contiguous bytes
-                    const int4 kk = *reinterpret_cast<const int4 *>(kr + d0);
-                    const int w4[4] = {kk.x, kk.y, kk.z, kk.w};
-                    float kf[16];
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) kf[i] = (float)(int8_t)(w4[i >> 2] >> (8 * (i & 3)));
+            for (int j = 0; j < 3; ++j) acc[bb][j] = v4i{0, 0, 0, 0};
 #pragma unroll
-                    for (int g = 0; g < GRP; ++g) {
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) part[g] = __builtin_fmaf(qr[g][d0 + 16 * qd + i], kf[i], part[g]);
+            for (int j = 0; j < 3; ++j) {
+                // volatile: read at its use each step, not hoisted out of the loop
+                const v4i qb = *reinterpret_cast<const volatile v4i *>(&qp[j][r16][16 * q4 + 64 * s]);
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+                    acc[bb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.a[bb][s], qb, acc[bb][j], 0, 0, 0);
+            }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * bb + i;
+                float x = (float)acc[bb][0][i] * s1;
+                x = __builtin_fmaf((float)acc[bb][1][i], s2, x);
+                x = __builtin_fmaf((float)acc[bb][2][i], s3, x);
+                sc[e] = (t8 + e < T) ? x * (ks[e] * 0.0625f) : -INFINITY;
+            }
+
+        // online softmax over the step (its first token is valid: mx is finite)
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = __builtin_fmaxf(mx, sc[e]);
+        mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mn = __builtin_fmaxf(m, mx);
+        const float alpha = expf(m - mn);                   // 0 on the first step
+        l = l * alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sc[e] = expf(sc[e] - mn);                       // invalid tokens: exp(-inf) = 0
+            l = l + sc[e];
+        }
+        m = mn;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+            for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[nb][i] = o[nb][i] * al[i];
+        }
+
+        // PV: A = weights (head r16, tokens ts + 8 q4 + e) as BF16 hi + lo,
+        // B = the V block of the same tokens; V slots past T zeroed
+        const int nv = T - (ts + 8 * q4);
+        uint32_t mk[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mk[c] = nv >= 2 * c + 2 ? 0xffffffffu : (nv == 2 * c + 1 ? 0x0000ffffu : 0u);
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a = sc[2 * c], d = sc[2 * c + 1];
+            hi[c] = pack_bf16x2(a, d);
+            lo[c] = pack_bf16x2(a - bf16_lo(hi[c]), d - bf16_hi(hi[c]));
+        }
+        const v8bf wh = __builtin_bit_cast(v8bf, hi), wl8 = __builtin_bit_cast(v8bf, lo);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+            uint4 v = vv[nb];
+            v.x &= mk[0]; v.y &= mk[1]; v.z &= mk[2]; v.w &= mk[3];
+            const v8bf bv = __builtin_bit_cast(v8bf, v);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, bv, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl8, bv, o[nb], 0, 0, 0);
+        }
+    }
+
+    // merge the four waves: M = max_w m_w, o = sum_w o_w e^(m_w - M) in the
+    // order 0, 1, 2, 3 (wave 0 starts at the chunk's first token, which is
+    // valid; a wave with no tokens has m = -inf and adds zero)
+    l = l + shfl_xor_f(l, 16);
+    l = l + shfl_xor_f(l, 32);
+    if (q4 == 0) {
+        wm[wave][r16] = m;
+        wl[wave][r16] = l;
+    }
+    __syncthreads();
+    float fo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = 4 * q4 + i;
+        const float M = __builtin_fmaxf(__builtin_fmaxf(wm[0][g], wm[1][g]), __builtin_fmaxf(wm[2][g], wm[3][g]));
+        fo[i] = expf(wm[wave][g] - M);
+    }
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int g = 4 * q4 + i;
+                    if (g < p.grp) {
+                        float &s = osum[g][16 * nb + r16];
+                        const float x = o[nb][i] * fo[i];
+                        s = (w == 0) ? x : s + x;
                     }
                 }
-            }
-#pragma unroll
-            for (int g = 0; g < GRP; ++g) {
-                part[g] = part[g] + shfl_xor_f(part[g], 1);
-                part[g] = part[g] + shfl_xor_f(part[g], 2);
-            }
-            if (qd == 0 && tt < p.T) {
-                const float sc = p.k_scale[cbase + tt] * 0.0625f;
-#pragma unroll
-                for (int g = 0; g < GRP; ++g) pw[g][tc] = part[g] * sc;
-            }
-        }
-    }
-    __syncthreads();
-    float s[GRP];
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) s[g] = valid ? pw[g][tl] : 0.0f;
-    __syncthreads();
-
-    // chunk softmax: maxima over the wave, then over the 4 waves
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) {
-        const float mw = wave_max_f(valid ? s[g] : -INFINITY);
-        if (lane == 0) red[wave][g] = mw;
-    }
-    __syncthreads();
-    float mx[GRP];
-#pragma unroll
-    for (int g = 0; g < GRP; ++g)
-        mx[g] = __builtin_fmaxf(__builtin_fmaxf(red[0][g], red[1][g]), __builtin_fmaxf(red[2][g], red[3][g]));
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) {
-        const float e = valid ? expf(s[g] - mx[g]) : 0.0f;
-        pw[g][tl] = e;
-        float l = e;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) l = l + shfl_xor_f(l, m);
-        if (lane == 0) red[wave][g] = l;
-    }
-    __syncthreads();
-
-    // PV over the wave's 64 tokens: lane = 32 hf + dl takes the tokens of
-    // parity hf and dimensions 8 dl .. 8 dl + 7 (16-byte V loads, two tokens
-    // per instruction); the two parities are added at the end
-    float o[GRP][8];
-#pragma unroll
-    for (int g = 0; g < GRP; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = 0.0f;
-    const int hf = lane >> 5, dl = lane & 31;
-    const int tw = chunk * kDecodeChunk + wave * 64;
-    const int nt = min(64, p.T - tw);
-    for (int j = hf; j < nt; j += 2) {
-        const uint4 r = *reinterpret_cast<const uint4 *>(p.vc + (cbase + tw + j) * 256 + 8 * dl);
-        const float v[8] = {bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y),
-                            bf16_lo(r.z), bf16_hi(r.z), bf16_lo(r.w), bf16_hi(r.w)};
-#pragma unroll
-        for (int g = 0; g < GRP; ++g) {
-            const float e = pw[g][wave * 64 + j];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[g][i] = __builtin_fmaf(e, v[i], o[g][i]);
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < GRP; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = o[g][i] + shfl_xor_f(o[g][i], 32);
-    // waves in order 0..3
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w && hf == 0) {
-#pragma unroll
-            for (int g = 0; g < GRP; ++g)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    osum[g][8 * dl + i] = (w == 0) ? o[g][i] : osum[g][8 * dl + i] + o[g][i];
         }
         __syncthreads();
     }
-    for (int g = wave; g < GRP; g += 4) {
-        const int h = hk * GRP + g;
-        float *dst = p.part + (((int64_t)b * p.Hq + h) * p.nchunk + chunk) * kPartStride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[4 * lane + i] = osum[g][4 * lane + i];
-        if (lane == 0) {
-            dst[256] = mx[g];
-            dst[257] = (red[0][g] + red[1][g]) + (red[2][g] + red[3][g]);
-        }
+    for (int idx = threadIdx.x; idx < p.grp * 256; idx += 256) {
+        const int g = idx >> 8, d = idx & 255;
+        p.part[(((int64_t)b * p.Hq + hk * p.grp + g) * p.nchunk + chunk) * kPartStride + d] = osum[g][d];
+    }
+    if (threadIdx.x < p.grp) {
+        const int g = threadIdx.x;
+        float *dst = p.part + (((int64_t)b * p.Hq + hk * p.grp + g) * p.nchunk + chunk) * kPartStride;
+        const float M = __builtin_fmaxf(__builtin_fmaxf(wm[0][g], wm[1][g]), __builtin_fmaxf(wm[2][g], wm[3][g]));
+        float L = 0.0f;
+        for (int w = 0; w < 4; ++w) L = L + wl[w][g] * expf(wm[w][g] - M);
+        dst[256] = M;
+        dst[257] = L;
     }
 }
 
-// Combines the chunk partials of one query head: M = max m_c,
-// L = sum l_c e^(m_c - M), O = (sum o_c e^(m_c - M)) / L.  Wave w sums the
-// chunks c = w, w + 4, ... in increasing order; the four wave sums are added
-// in the order 0, 1, 2, 3 (a fixed order: the result is deterministic).
-// Grid (Hq, B), 256 threads.
-__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams p) {
-    __shared__ float wm[4];
-    __shared__ float wl[4];
-    __shared__ float wo[4][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = blockIdx.x, b = blockIdx.y;
-    const float *src = p.part + ((int64_t)b * p.Hq + h) * p.nchunk * kPartStride;
-    float M = -INFINITY;
-    for (int c = threadIdx.x; c < p.nchunk; c += 256) M = __builtin_fmaxf(M, src[c * kPartStride + 256]);
-    M = wave_max_f(M);
-    if (lane == 0) wm[wave] = M;
-    __syncthreads();
-    M = __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3]));
-    float L = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = wave; c < p.nchunk; c += 4) {
-        const float *pc = src + c * kPartStride;
-        const float4 x = *reinterpret_cast<const float4 *>(pc + 4 * lane);
-        const float f = expf(pc[256] - M);
-        L = __builtin_fmaf(pc[257], f, L);
-        o[0] = __builtin_fmaf(x.x, f, o[0]);
-        o[1] = __builtin_fmaf(x.y, f, o[1]);
-        o[2] = __builtin_fmaf(x.z, f, o[2]);
-        o[3] = __builtin_fmaf(x.w, f, o[3]);
+// Combines the chunk partials of one query head: M = max_c m_c,
+// f_c = e^(m_c - M), L = sum_c l_c f_c, O = (sum_c o_c f_c) / L.  Thread
+// (group cg, channel d) of the 1024 sums o_c[d] f_c over the chunks c = cg,
+// cg + 4, ... in increasing order; the four group sums are added in the order
+// 0, 1, 2, 3, and L is summed in increasing c (a fixed order: the result is
+// deterministic).  The first partials a thread needs are loaded together with
+// the maxima, so a short combine takes one round trip to memory.
+// Grid (Hq, B), 1024 threads.
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineChunks = 1024;    // chunks whose weights one pass keeps in LDS
+constexpr int kCombineAhead = 8;        // partials per thread loaded before the maximum
+
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeParams p) {
+    __shared__ float wmax[kCombineThreads / 64];
+    __shared__ float fw[kCombineChunks];
+    __shared__ float lw[kCombineChunks];
+    __shared__ float og[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+    const int d = tid & 255, cg = tid >> 8;
+    const int h = blockIdx.x, b = blockIdx.y, nchunk = p.nchunk;
+    const float *src = p.part + ((int64_t)b * p.Hq + h) * nchunk * kPartStride;
+
+    float pv[kCombineAhead];
+#pragma unroll
+    for (int i = 0; i < kCombineAhead; ++i) {
+        const int c = cg + 4 * i;
+        pv[i] = c < nchunk ? src[(int64_t)c * kPartStride + d] : 0.0f;
     }
-    if (lane == 0) wl[wave] = L;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wo[wave][4 * lane + i] = o[i];
+    float mc = -INFINITY, lc = 0.0f;
+    if (tid < nchunk) {
+        mc = src[(int64_t)tid * kPartStride + 256];
+        lc = src[(int64_t)tid * kPartStride + 257];
+    }
+    float M = mc;
+    for (int c = tid + kCombineThreads; c < nchunk; c += kCombineThreads)
+        M = __builtin_fmaxf(M, src[(int64_t)c * kPartStride + 256]);
+    M = wave_max_f(M);
+    if (lane == 0) wmax[wave] = M;
     __syncthreads();
-    if (wave == 0) {
-        const float Lt = ((wl[0] + wl[1]) + wl[2]) + wl[3];
-        const float r = 1.0f / Lt;
-        float t[4];
+    M = wmax[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            t[i] = (((wo[0][4 * lane + i] + wo[1][4 * lane + i]) + wo[2][4 * lane + i]) + wo[3][4 * lane + i]) * r;
-        uint16_t *dst = p.o + ((int64_t)b * p.Hq + h) * 256 + 4 * lane;
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]));
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = __builtin_fmaxf(M, wmax[w]);
+
+    float L = 0.0f, o = 0.0f;
+    for (int c0 = 0; c0 < nchunk; c0 += kCombineChunks) {
+        const int nc = min(kCombineChunks, nchunk - c0);
+        if (c0 > 0) {
+            __syncthreads();                // the previous pass's weights are consumed
+            if (tid < nc) {
+                mc = src[(int64_t)(c0 + tid) * kPartStride + 256];
+                lc = src[(int64_t)(c0 + tid) * kPartStride + 257];
+            }
+        }
+        if (tid < nc) {
+            fw[tid] = expf(mc - M);
+            lw[tid] = lc;
+        }
+        __syncthreads();
+        int c = cg;
+        if (c0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kCombineAhead; ++i, c += 4)
+                if (c < nc) o = __builtin_fmaf(pv[i], fw[c], o);
+        }
+#pragma unroll 8
+        for (; c < nc; c += 4) o = __builtin_fmaf(src[(int64_t)(c0 + c) * kPartStride + d], fw[c], o);
+        if (tid == 0)
+            for (int k = 0; k < nc; ++k) L = __builtin_fmaf(lw[k], fw[k], L);
+    }
+    og[cg][d] = o;
+    __syncthreads();
+    if (tid == 0) wmax[0] = L;
+    __syncthreads();
+    if (cg == 0) {
+        const float t = (((og[0][d] + og[1][d]) + og[2][d]) + og[3][d]) * (1.0f / wmax[0]);
+        const float u = __shfl_xor(t, 1, 64);               // pairs of channels -> one BF16x2 store
+        if ((d & 1) == 0) {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(p.o + ((int64_t)b * p.Hq + h) * 256 + d);
+            *dst = pack_bf16x2(t, u);
+        }
     }
 }
 
@@ -270,23 +469,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams 
 }  // namespace sage
 
 hipError_t sage_launch_kv_append(const sage::KvAppendParams &p, hipStream_t s) {
-    const unsigned rows = (unsigned)p.n * (unsigned)p.Hkv;
-    sage::kv_append_kernel<<<dim3((rows + 3) / 4, p.B), 256, 0, s>>>(p);
+    const unsigned items = (unsigned)p.nblk * (unsigned)p.Hkv;
+    sage::kv_append_kernel<<<dim3((items + 3) / 4, p.B), 256, 0, s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t sage_launch_decode(const sage::DecodeParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.nchunk * p.Hkv), p.B);
-    switch (p.grp) {
-    case 1: sage::decode_chunk_kernel<1><<<grid, 256, 0, s>>>(p); break;
-    case 2: sage::decode_chunk_kernel<2><<<grid, 256, 0, s>>>(p); break;
-    case 4: sage::decode_chunk_kernel<4><<<grid, 256, 0, s>>>(p); break;
-    case 8: sage::decode_chunk_kernel<8><<<grid, 256, 0, s>>>(p); break;
-    case 16: sage::decode_chunk_kernel<16><<<grid, 256, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-    }
+    if (p.grp < 1 || p.grp > sage::kDecodeMaxGroup) return hipErrorInvalidValue;
+    sage::decode_chunk_kernel<<<dim3((unsigned)(p.nchunk * p.Hkv), p.B), 256, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sage::decode_combine_kernel<<<dim3(p.Hq, p.B), 256, 0, s>>>(p);
+    sage::decode_combine_kernel<<<dim3(p.Hq, p.B), sage::kCombineThreads, 0, s>>>(p);
     return hipGetLastError();
 }

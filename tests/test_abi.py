@@ -144,17 +144,18 @@ def test_decode_cache_refusals_happen_before_launch(sage):
     assert append(cache(), -1, 1) == "SAGE_E_SHAPE"
     assert append(cache(), 0, 0) == "SAGE_E_SHAPE"
     assert append(cache(v=A + 4), 0, 1) == "SAGE_E_ALIGN"
+    assert append(cache(capacity=60), 0, 1) == "SAGE_E_SHAPE"   # capacity not a multiple of 8
     assert append(cache(), 0, 1, SageView(A, 0, 512, 256, 2)) == "SAGE_E_STRIDE"
     n = ctypes.c_size_t()
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 64, ctypes.byref(n))) == "SAGE_OK"
-    assert n.value == 1 * 8 * 1 * 260 * 4 + (-(1 * 8 * 260 * 4) % 256)
+    assert n.value == 1 * 8 * 1 * 260 * 4 + (-(1 * 8 * 260 * 4) % 256)     # one chunk of partials
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 65, ctypes.byref(n))) == "SAGE_E_SHAPE"
     q = SageView(A, 0, 8 * 256, 256, 1)
     attn = lambda c, Hq, T, ws=A, wsb=1 << 30, o=A: name(lib.sage_decode_attn(
         ctypes.byref(c), Hq, ctypes.byref(q), T, o, ws, wsb, None))
     assert attn(cache(), 8, 64, o=None) == "SAGE_E_NULL"
     assert attn(cache(), 7, 64) == "SAGE_E_GQA"
-    assert attn(cache(), 6, 64) == "SAGE_E_UNSUPPORTED"       # 3 query heads per KV head
+    assert attn(cache(), 34, 64) == "SAGE_E_UNSUPPORTED"      # 17 query heads per KV head
     assert attn(cache(), 8, 0) == "SAGE_E_SHAPE"
     assert attn(cache(), 8, 65) == "SAGE_E_SHAPE"
     assert attn(cache(), 8, 64, wsb=16) == "SAGE_E_WORKSPACE"

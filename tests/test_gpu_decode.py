@@ -28,9 +28,12 @@ def _kv(rng, B, n, Hkv, scale=1.0):
     return buf, k, v
 
 
-def _cache_host(cache, T):
-    return (cache.k8[:, :, :T].cpu().numpy(), cache.k_scale[:, :, :T].cpu().numpy(),
-            cache.v[:, :, :T].cpu().view(torch.int16).numpy().view(np.uint16))
+def _cache_k_host(cache, T):
+    return cache.k8[:, :, :T].cpu().numpy(), cache.k_scale[:, :, :T].cpu().numpy()
+
+
+def _v_bits(t):
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
 def test_append_matches_oracle_byte_for_byte():
@@ -44,12 +47,16 @@ def test_append_matches_oracle_byte_for_byte():
     dv = dbuf[:, :, (Hkv + 1) * D:].view(B, n, Hkv, D)
     cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
     cache.k8.fill_(0x55)
+    cache.v.view(torch.int16).fill_(0x3f80)            # BF16 1.0 in every slot before the append
     sage.kv_append(cache, dk, dv, t0)
     torch.cuda.synchronize()
     k8, ks = oracle.kv_quant(k)
     assert np.array_equal(cache.k8[:, :, t0:t0 + n].cpu().numpy(), k8)
     assert np.array_equal(cache.k_scale[:, :, t0:t0 + n].cpu().numpy().view(np.uint32), ks.view(np.uint32))
-    assert torch.equal(cache.v[:, :, t0:t0 + n].cpu().view(torch.int16), v.permute(0, 2, 1, 3).view(torch.int16))
+    vr = _v_bits(cache.v_rows())
+    assert np.array_equal(vr[:, :, t0:t0 + n], _v_bits(v.permute(0, 2, 1, 3)))
+    # the other tokens of the partly written 8-token blocks (and all others) keep their values
+    assert (vr[:, :, :t0] == 0x3f80).all() and (vr[:, :, t0 + n:] == 0x3f80).all()
     assert (cache.k8[:, :, :t0] == 0x55).all() and (cache.k8[:, :, t0 + n:] == 0x55).all()
 
 
@@ -70,18 +77,22 @@ def test_append_in_pieces_equals_one_append():
     assert torch.equal(a.v.view(torch.int16), b.v.view(torch.int16))
 
 
-def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label=""):
+def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label="", poison=False):
     import quantized_exact_order_amd as sage
     rng = np.random.default_rng(seed)
-    banner(f"decode {label} B={B} Hq={Hq} Hkv={Hkv} T={T}")
+    banner(f"decode {label} B={B} Hq={Hq} Hkv={Hkv} T={T} cap={cap}")
     _, k, v = _kv(rng, B, T, Hkv)
     q = torch.from_numpy((rng.standard_normal((B, Hq, D)) * q_scale).astype(np.float32)).to(torch.bfloat16)
     cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
+    if poison:          # NaN in every V slot, K scale and K byte pattern that the append does not write
+        cache.v.view(torch.int16).fill_(0x7fc0)
+        cache.k_scale.view(torch.int32).fill_(0x7fc00000)
+        cache.k8.fill_(-128)
     sage.kv_append(cache, k.cuda(), v.cuda(), 0)
     o = sage.decode_attn(cache, q.cuda(), T)
     torch.cuda.synchronize()
-    k8, ks, vc = _cache_host(cache, T)
-    o_ref, _ = oracle.decode_attn(q, k8, ks, vc, T)
+    k8, ks = oracle.kv_quant(k)
+    o_ref, _ = oracle.decode_attn(q, k8, ks, _v_bits(v.permute(0, 2, 1, 3)), T)
     g = o.cpu().float().numpy().astype(np.float64)
     r = oracle.bf16_to_f32(o_ref).astype(np.float64)
     err = np.abs(g - r)
@@ -91,14 +102,20 @@ def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label=""):
     assert oracle.cosine(g, r) >= 0.99999
 
 
-@pytest.mark.parametrize("Hq", [2, 4, 8, 16, 32])
+@pytest.mark.parametrize("Hq", [2, 4, 6, 8, 16, 26, 32])
 def test_decode_group_sizes(Hq):
     _check_decode(2, Hq, 2, 300, 320, seed=30 + Hq, label=f"grp {Hq // 2}")
 
 
-@pytest.mark.parametrize("T", [1, 2, 63, 64, 255, 256, 257, 511, 513, 1000])
+@pytest.mark.parametrize("T", [1, 2, 7, 9, 31, 33, 63, 64, 255, 256, 257, 511, 513, 1000])
 def test_decode_token_counts(T):
     _check_decode(1, 8, 2, T, 1024, seed=40 + T, q_scale=2.0, label=f"T={T}")
+
+
+@pytest.mark.parametrize("T,cap", [(1, 8), (13, 16), (300, 304), (296, 296), (777, 1024)])
+def test_decode_ignores_unwritten_cache_slots(T, cap):
+    # slots past T hold NaN; the last chunk reaches past the capacity when T = cap
+    _check_decode(2, 16, 2, T, cap, seed=70 + T, q_scale=2.0, label="poisoned", poison=True)
 
 
 @pytest.mark.timeout(300)
@@ -121,7 +138,7 @@ def test_kld_gate_on_gpu_cache(mult):
         cache = sage.KvCache.allocate(1, 1, 512, "cuda")
         sage.kv_append(cache, k.cuda(), k.cuda(), 0)
         torch.cuda.synchronize()
-        k8, ks, _ = _cache_host(cache, 512)
+        k8, ks = _cache_k_host(cache, 512)
         kd = k8[0, 0].astype(np.float64) * ks[0, 0, :, None].astype(np.float64)
         qr = HM @ q.float().numpy().astype(np.float64)
         s_q = kd @ qr / math.sqrt(D)

@@ -81,6 +81,7 @@ def lib():
         L.oracle_quant_v.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
         L.oracle_attn_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P]
         L.oracle_attn_rows_mode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, P, i32]
+        L.oracle_attn_rows_segmented.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, i32, P]
         L.oracle_kv_quant.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
         L.oracle_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_f64_to_f16.restype = f32
@@ -268,6 +269,31 @@ def attn_rows(p: Prepared, rows: np.ndarray, pv_fp16: bool = False) -> np.ndarra
                                 _ptr(p.k_scale), _ptr(p.v8), _ptr(p.v_scale), rows.shape[0],
                                 _ptr(rows), _ptr(o), int(bool(pv_fp16)))
     return o
+
+
+def attn_rows_segmented(p: Prepared, rows: np.ndarray, nseg: int) -> np.ndarray:
+    """Output of the segmented (split-KV, non-exact) schedule with nseg
+    segments of key tiles, for rows (b, h, i); uint16 BF16 [len(rows), D]."""
+    B, Hq, N, D = p.q8.shape
+    Hkv = p.k8.shape[1]
+    nk = (N + 63) // 64
+    if not 1 <= nseg <= nk:
+        raise ValueError(f"nseg must be in [1, {nk}]")
+    rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 3)
+    o = np.empty((rows.shape[0], D), np.uint16)
+    if rows.shape[0] == 0:
+        return o
+    lib().oracle_attn_rows_segmented(B, N, Hq, Hkv, D, _ptr(p.q8), _ptr(p.q_scale), _ptr(p.k8),
+                                     _ptr(p.k_scale), _ptr(p.v8), _ptr(p.v_scale), rows.shape[0],
+                                     _ptr(rows), int(nseg), _ptr(o))
+    return o
+
+
+def attention_segmented(p: Prepared, nseg: int) -> np.ndarray:
+    """attn_rows_segmented over every row, as BF16 bits [B, N, Hq, D]."""
+    B, Hq, N, D = p.q8.shape
+    o = attn_rows_segmented(p, all_rows(B, Hq, N), nseg)
+    return o.reshape(B, Hq, N, D).transpose(0, 2, 1, 3).copy()
 
 
 def f64_to_f16(x: float) -> float:

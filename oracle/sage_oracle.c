@@ -390,6 +390,116 @@ void oracle_quant_v(int B, int N, int H, int D, const uint16_t *v, int64_t sb, i
 /* Attention                                                                 */
 /* ------------------------------------------------------------------------ */
 
+/* Operands of query row (b, h, i): its INT8 row and Q-group scale, and the
+ * K, V, K-scale and V-scale arrays of its KV head h / (Hq / Hkv). */
+struct row_operands {
+    const int8_t *qi, *kb;
+    const uint8_t *vb;
+    const float *ks, *vs;
+    float qs;
+};
+
+static struct row_operands row_operands_of(int N, int Hq, int Hkv, int D, const int8_t *q8,
+                                           const float *q_scale, const int8_t *k8, const float *k_scale,
+                                           const uint8_t *v8, const float *v_scale, int b, int h, int i)
+{
+    const int nq = ((N + 127) / 128) * 4;
+    const int nk = (N + 63) / 64;
+    const int grp = Hq / Hkv;
+    struct row_operands r;
+    int hk = h / grp;
+    r.qi = q8 + (((int64_t)b * Hq + h) * N + i) * D;
+    r.qs = q_scale[((int64_t)b * Hq + h) * nq + i / 32];
+    r.kb = k8 + ((int64_t)b * Hkv + hk) * N * D;
+    r.vb = v8 + ((int64_t)b * Hkv + hk) * N * D;
+    r.ks = k_scale + ((int64_t)b * Hkv + hk) * nk;
+    r.vs = v_scale + ((int64_t)b * Hkv + hk) * D;
+    return r;
+}
+
+/* The per-tile steps for key tiles t0 .. t1-1 in increasing order, from the
+ * state (RO, m, d); T is scratch of D floats.  The steps are listed with
+ * oracle_attn_rows_mode below. */
+static void attn_tiles(const struct row_operands *r, int N, int D, float c, const float *dec, int t0, int t1,
+                       int pv_fp16, float *RO, float *T, float *m_io, float *d_io)
+{
+    const int8_t *qi = r->qi, *kb = r->kb;
+    const uint8_t *vb = r->vb;
+    const float *ks = r->ks;
+    const float qs = r->qs;
+    int32_t S[64];
+    float sv[64];
+    uint8_t p8[64];
+    float m = *m_io, d = *d_io;
+    for (int t = t0; t < t1; t++) {
+        float f = (qs * c) * ks[t];
+        float mx = -INFINITY;
+        for (int j = 0; j < 64; j++) {
+            int key = t * 64 + j;
+            if (key < N) {
+                int32_t acc = 0;
+                for (int e = 0; e < D; e++)
+                    acc += (int32_t)qi[e] * (int32_t)kb[(int64_t)key * D + e];
+                S[j] = acc;
+                sv[j] = (float)acc * f;
+            } else {
+                S[j] = 0;
+                sv[j] = -5000000.0f;
+            }
+            if (sv[j] > mx) mx = sv[j];
+        }
+        float M = mx - 8.807f;
+        float mn = (m > M) ? m : M;
+        float alpha = oracle_exp2(m - mn);
+        d = d * alpha;
+        for (int e = 0; e < D; e++) RO[e] = RO[e] * alpha;
+        for (int j = 0; j < 64; j++) {
+            int key = t * 64 + j;
+            float p = (key < N) ? oracle_exp2(fmaf((float)S[j], f, -mn)) : 0.0f;
+            d = d + p;
+            p8[j] = oracle_f32_to_e4m3(p);
+        }
+        if (!pv_fp16) {
+            for (int e = 0; e < D; e++) T[e] = 0.0f;
+            for (int j = 0; j < 64; j++) {
+                int key = t * 64 + j;
+                if (key >= N) continue;           /* invalid V rows are zero */
+                float pj = dec[p8[j]];
+                const uint8_t *vr = vb + (int64_t)key * D;
+                for (int e = 0; e < D; e++) T[e] = T[e] + pj * dec[vr[e]];
+            }
+        } else {
+            /* two ordered K=32 steps into an FP16 fragment: each step adds
+             * its 32 exact products (exact in double) to the fragment and
+             * rounds once to FP16 */
+            for (int e = 0; e < D; e++) {
+                double frag = 0.0;
+                for (int half = 0; half < 2; half++) {
+                    double acc = frag;
+                    for (int j = 32 * half; j < 32 * half + 32; j++) {
+                        int key = t * 64 + j;
+                        if (key >= N) continue;
+                        acc += (double)dec[p8[j]] * (double)dec[vb[(int64_t)key * D + e]];
+                    }
+                    frag = (double)oracle_f64_to_f16(acc);
+                }
+                T[e] = (float)frag;
+            }
+        }
+        for (int e = 0; e < D; e++) RO[e] = RO[e] + T[e];
+        m = mn;
+    }
+    *m_io = m;
+    *d_io = d;
+}
+
+/* O = bf16((RO * (1/d)) * v_scale) ("Finalization And Tails"). */
+static void finalize_row(const float *RO, float d, const float *vs, int D, uint16_t *o)
+{
+    float rcp = 1.0f / d;
+    for (int e = 0; e < D; e++) o[e] = oracle_f32_to_bf16((RO[e] * rcp) * vs[e]);
+}
+
 /*
  * Quantized attention for a list of query rows ("INT8 QK And Score Domain",
  * "Online Softmax", "V And PV", "Finalization And Tails").
@@ -424,91 +534,81 @@ void oracle_attn_rows_mode(int B, int N, int Hq, int Hkv, int D,
                            const uint8_t *v8, const float *v_scale,
                            int64_t nrows, const int32_t *rows, uint16_t *o, int pv_fp16)
 {
-    const int nq = ((N + 127) / 128) * 4;
     const int nk = (N + 63) / 64;
-    const int grp = Hq / Hkv;
     const float c = oracle_score_scale(D);
     float dec[256];
     for (int i = 0; i < 256; i++) dec[i] = oracle_e4m3_to_f32((uint8_t)i);
 
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = 0; r < nrows; r++) {
-        int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
-        int hk = h / grp;
-        const int8_t *qi = q8 + (((int64_t)b * Hq + h) * N + i) * D;
-        float qs = q_scale[((int64_t)b * Hq + h) * nq + i / 32];
-        const int8_t *kb = k8 + ((int64_t)b * Hkv + hk) * N * D;
-        const uint8_t *vb = v8 + ((int64_t)b * Hkv + hk) * N * D;
-        const float *ks = k_scale + ((int64_t)b * Hkv + hk) * nk;
-        const float *vs = v_scale + ((int64_t)b * Hkv + hk) * D;
-
+        struct row_operands ro = row_operands_of(N, Hq, Hkv, D, q8, q_scale, k8, k_scale, v8, v_scale,
+                                                 rows[3 * r], rows[3 * r + 1], rows[3 * r + 2]);
         float *RO = (float *)calloc(D, sizeof(float));
         float *T = (float *)malloc(sizeof(float) * D);
-        int32_t S[64];
-        float sv[64];
-        uint8_t p8[64];
         float m = -5000000.0f, d = 1.0f;
-        for (int t = 0; t < nk; t++) {
-            float f = (qs * c) * ks[t];
-            float mx = -INFINITY;
-            for (int j = 0; j < 64; j++) {
-                int key = t * 64 + j;
-                if (key < N) {
-                    int32_t acc = 0;
-                    for (int e = 0; e < D; e++)
-                        acc += (int32_t)qi[e] * (int32_t)kb[(int64_t)key * D + e];
-                    S[j] = acc;
-                    sv[j] = (float)acc * f;
-                } else {
-                    S[j] = 0;
-                    sv[j] = -5000000.0f;
-                }
-                if (sv[j] > mx) mx = sv[j];
-            }
-            float M = mx - 8.807f;
-            float mn = (m > M) ? m : M;
-            float alpha = oracle_exp2(m - mn);
-            d = d * alpha;
-            for (int e = 0; e < D; e++) RO[e] = RO[e] * alpha;
-            for (int j = 0; j < 64; j++) {
-                int key = t * 64 + j;
-                float p = (key < N) ? oracle_exp2(fmaf((float)S[j], f, -mn)) : 0.0f;
-                d = d + p;
-                p8[j] = oracle_f32_to_e4m3(p);
-            }
-            if (!pv_fp16) {
-                for (int e = 0; e < D; e++) T[e] = 0.0f;
-                for (int j = 0; j < 64; j++) {
-                    int key = t * 64 + j;
-                    if (key >= N) continue;           /* invalid V rows are zero */
-                    float pj = dec[p8[j]];
-                    const uint8_t *vr = vb + (int64_t)key * D;
-                    for (int e = 0; e < D; e++) T[e] = T[e] + pj * dec[vr[e]];
-                }
-            } else {
-                /* two ordered K=32 steps into an FP16 fragment: each step adds
-                 * its 32 exact products (exact in double) to the fragment and
-                 * rounds once to FP16 */
-                for (int e = 0; e < D; e++) {
-                    double frag = 0.0;
-                    for (int half = 0; half < 2; half++) {
-                        double acc = frag;
-                        for (int j = 32 * half; j < 32 * half + 32; j++) {
-                            int key = t * 64 + j;
-                            if (key >= N) continue;
-                            acc += (double)dec[p8[j]] * (double)dec[vb[(int64_t)key * D + e]];
-                        }
-                        frag = (double)oracle_f64_to_f16(acc);
-                    }
-                    T[e] = (float)frag;
-                }
-            }
-            for (int e = 0; e < D; e++) RO[e] = RO[e] + T[e];
-            m = mn;
-        }
-        float rcp = 1.0f / d;
-        for (int e = 0; e < D; e++) o[r * D + e] = oracle_f32_to_bf16((RO[e] * rcp) * vs[e]);
+        attn_tiles(&ro, N, D, c, dec, 0, nk, pv_fp16, RO, T, &m, &d);
+        finalize_row(RO, d, ro.vs, D, o + r * D);
         free(RO);
+        free(T);
+    }
+}
+
+/*
+ * Segmented (split-KV) schedule: an opt-in mode that is NOT the contract's
+ * exact order (the contract forbids combining KV partials; the FP8-PV
+ * page's segmented schedule is the model).  The nseg segments split the key
+ * tiles [0, nk) into contiguous runs, segment s covering tiles
+ * [s nk / nseg, (s + 1) nk / nseg) (integer division; 1 <= nseg <= nk, so no
+ * run is empty).  Each segment runs the per-tile steps above from the
+ * initial state (RO = 0, m = -5e6, d = 1) over its tiles, giving
+ * (RO_s, m_s, d_s).  The segments are then combined in increasing s:
+ *   M = max_s m_s,  a_s = exp2(m_s - M)  (the softmax's exp2),
+ *   d = sum_s d_s * a_s,  RO[e] = sum_s RO_s[e] * a_s  (FP32, from 0, in order),
+ * and O is finalized as in the exact path.  With nseg = 1 the combine is the
+ * identity (a_0 = 1), so the result is the exact path's.
+ * Pinned by: nseg = 1 against the exact oracle, the zero-query and one-hot
+ * closed forms at every segmentation, FP64 attention on the dequantized
+ * tensors.
+ */
+void oracle_attn_rows_segmented(int B, int N, int Hq, int Hkv, int D,
+                                const int8_t *q8, const float *q_scale,
+                                const int8_t *k8, const float *k_scale,
+                                const uint8_t *v8, const float *v_scale,
+                                int64_t nrows, const int32_t *rows, int nseg, uint16_t *o)
+{
+    const int nk = (N + 63) / 64;
+    const float c = oracle_score_scale(D);
+    float dec[256];
+    for (int i = 0; i < 256; i++) dec[i] = oracle_e4m3_to_f32((uint8_t)i);
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; r++) {
+        struct row_operands ro = row_operands_of(N, Hq, Hkv, D, q8, q_scale, k8, k_scale, v8, v_scale,
+                                                 rows[3 * r], rows[3 * r + 1], rows[3 * r + 2]);
+        float *ROs = (float *)calloc((size_t)nseg * D, sizeof(float));
+        float *ms = (float *)malloc(sizeof(float) * nseg);
+        float *ds = (float *)malloc(sizeof(float) * nseg);
+        float *T = (float *)malloc(sizeof(float) * D);
+        for (int s = 0; s < nseg; s++) {
+            int t0 = (int)((int64_t)s * nk / nseg), t1 = (int)((int64_t)(s + 1) * nk / nseg);
+            ms[s] = -5000000.0f;
+            ds[s] = 1.0f;
+            attn_tiles(&ro, N, D, c, dec, t0, t1, 0, ROs + (int64_t)s * D, T, &ms[s], &ds[s]);
+        }
+        float M = ms[0];
+        for (int s = 1; s < nseg; s++) M = (ms[s] > M) ? ms[s] : M;
+        float *RO = T;
+        float d = 0.0f;
+        for (int e = 0; e < D; e++) RO[e] = 0.0f;
+        for (int s = 0; s < nseg; s++) {
+            float a = oracle_exp2(ms[s] - M);
+            d = d + ds[s] * a;
+            for (int e = 0; e < D; e++) RO[e] = RO[e] + ROs[(int64_t)s * D + e] * a;
+        }
+        finalize_row(RO, d, ro.vs, D, o + r * D);
+        free(ROs);
+        free(ms);
+        free(ds);
         free(T);
     }
 }

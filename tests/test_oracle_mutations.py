@@ -23,7 +23,8 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 PIN_FILES = ["tests/test_oracle_formats.py", "tests/test_oracle_prep.py", "tests/test_oracle_attn.py",
-             "tests/test_oracle_decode.py", "tests/test_oracle_pv16.py", "tests/test_golden_boundary.py"]
+             "tests/test_oracle_segmented.py", "tests/test_oracle_decode.py", "tests/test_oracle_pv16.py",
+             "tests/test_golden_boundary.py"]
 
 # (name, pin file run first, exact text in sage_oracle.c, replacement)
 MUTANTS = [
@@ -68,12 +69,18 @@ MUTANTS = [
     ("attn_no_fp8_offset", "attn", "float M = mx - 8.807f;", "float M = mx;"),
     ("attn_no_rescale", "attn", "for (int e = 0; e < D; e++) RO[e] = RO[e] * alpha;", ""),
     ("attn_no_v_scale", "attn", "oracle_f32_to_bf16((RO[e] * rcp) * vs[e]);", "oracle_f32_to_bf16(RO[e] * rcp);"),
-    ("attn_gqa_modulo", "attn", "        int hk = h / grp;\n", "        int hk = h % Hkv;\n"),
+    ("attn_gqa_modulo", "attn", "    int hk = h / grp;\n", "    int hk = h % Hkv;\n"),
     ("attn_invalid_keys_in_denominator", "attn",
      "float p = (key < N) ? oracle_exp2(fmaf((float)S[j], f, -mn)) : 0.0f;",
      "float p = oracle_exp2(fmaf((float)S[j], f, -mn));"),
     ("attn_first_tile_scale_only", "attn", "float f = (qs * c) * ks[t];", "float f = (qs * c) * ks[0];"),
     ("attn_fp16_partial_not_rounded", "pv16", "frag = (double)oracle_f64_to_f16(acc);", "frag = acc;"),
+    # segmented (split-KV) schedule
+    ("seg_combine_d_unweighted", "segmented", "d = d + ds[s] * a;", "d = d + ds[s];"),
+    ("seg_combine_ro_unweighted", "segmented", "RO[e] = RO[e] + ROs[(int64_t)s * D + e] * a;",
+     "RO[e] = RO[e] + ROs[(int64_t)s * D + e];"),
+    ("seg_overlapping_runs", "segmented", "int t0 = (int)((int64_t)s * nk / nseg), t1",
+     "int t0 = (int)((int64_t)s * nk / nseg) - (s > 0), t1"),
     # decode cache
     ("kv_cache_skips_rotation", "decode", "oracle_wht(u, D);\n                int64_t r", "int64_t r"),
     ("decode_query_not_rotated", "decode", "oracle_wht(qr, D);", ""),

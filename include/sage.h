@@ -147,6 +147,28 @@ sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, cons
 sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
                           int64_t osn, int64_t osh, void *stream);
 
+/* Segmented (split-KV) attention: an opt-in mode that is NOT the exact order
+ * of sage_attn_fwd.  The contract page forbids combining KV partials; this
+ * mode combines them, after the FP8-PV page's segmented schedules, to give
+ * short sequences more work-groups.  The key tiles [0, nk) (nk = ceil(N/64))
+ * are split into nseg contiguous runs, run s covering tiles
+ * [s*nk/nseg, (s+1)*nk/nseg); each run performs the per-tile steps of
+ * sage_attn_fwd from the initial state (RO = 0, m = -5e6, d = 1), and the
+ * runs are combined in increasing s: M = max m_s, a_s = exp2(m_s - M),
+ * d = sum d_s a_s, RO = sum RO_s a_s, O = bf16((RO * (1/d)) * v_scale).
+ * With nseg = 1 the result is bit-identical to sage_attn_fwd.
+ *   nseg       1 <= nseg <= ceil(N/64)
+ *   o, osb, osn, osh   as for sage_attn_fwd
+ *   workspace  device memory of at least sage_attn_segmented_workspace bytes,
+ *              16-byte aligned: the runs' FP32 partials (RO, m, d)
+ * Refusals: those of sage_attn_fwd, SAGE_E_SHAPE (nseg out of range, or
+ * B * Hq * nseg * ceil(N/128) >= 2^31 work-groups), SAGE_E_WORKSPACE,
+ * SAGE_E_ALIGN (workspace). */
+sage_status sage_attn_segmented_workspace(const sage_shape *shape, int32_t nseg, size_t *bytes);
+sage_status sage_attn_fwd_segmented(const sage_shape *shape, const sage_bufs *bufs, int32_t nseg, void *o,
+                                    int64_t osb, int64_t osn, int64_t osh, void *workspace, size_t ws_bytes,
+                                    void *stream);
+
 /* ------------------------------------------------------------------------
  * Decode-time INT8 K cache (the NPU issue page on INT8 KV with per-head
  * Hadamard rotation, part A, the variant with INT8 K and 16-bit V): every K

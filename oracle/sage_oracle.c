@@ -10,7 +10,8 @@
  * "Online Softmax", "V And PV", "Finalization And Tails".  Where that page is
  * silent the reading used is stated next to the step.  The Walsh-Hadamard
  * variant follows the NPU issue page on INT8 KV with per-head Hadamard
- * rotation ("rotation is free on the K side", ordering risk).
+ * rotation (the rotation costs nothing on the K side; its place in the
+ * order of steps is the page's stated risk).
  *
  * Arithmetic conventions: every + - * / sqrt is IEEE binary32 with
  * round-to-nearest-even; the file is compiled with -ffp-contract=off, so no
@@ -38,8 +39,8 @@ static uint32_t bits_of_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; 
 /* BF16 storage -> FP32 value (exact widening).  Pinned by: torch bf16 decode. */
 float oracle_bf16_to_f32(uint16_t h) { return f32_of_bits((uint32_t)h << 16); }
 
-/* FP32 -> BF16, round to nearest, ties to even ("round ... to BF16 RN",
- * Preparation).  Adding 0x7FFF plus the kept LSB to the 32-bit pattern and
+/* FP32 -> BF16, round to nearest, ties to even (the rounding the page fixes
+ * for BF16, section "Preparation").  Adding 0x7FFF plus the kept LSB to the 32-bit pattern and
  * truncating is the usual exact RNE on the binary encoding (a carry into the
  * exponent gives the next binade or infinity, as rounding requires).
  * NaN keeps its sign and becomes quiet.  Pinned by: torch's conversion. */
@@ -65,8 +66,8 @@ float oracle_e4m3_to_f32(uint8_t c)
 }
 
 /* FP32 -> OCP E4M3, round to nearest even, saturate finite overflow to +-448
- * ("Convert probabilities FP32 to E4M3 RN, saturate-finite" and the V cast,
- * page sections "Online Softmax" and "V And PV").  NaN -> 0x7F/0xFF.
+ * (the page converts probabilities and V this way, sections "Online
+ * Softmax" and "V And PV").  NaN -> 0x7F/0xFF.
  * The value is scaled by a power of two so that the code's last mantissa step
  * is 1, rounded with rint() in double (exact, default mode is to-nearest-even)
  * and re-encoded.  Pinned by: torch float8_e4m3fn below 448, format facts. */
@@ -102,10 +103,11 @@ int8_t oracle_f32_to_i8(float x)
     return (int8_t)r;
 }
 
-/* 2^x for the softmax ("ex2.approx.ftz.f32" on the page).  The oracle does
- * not imitate an approximate instruction: it takes exp2 in FP64, rounds once
- * to FP32, and flushes results below the smallest normal to zero (the ftz of
- * the page).  Pinned by: numpy exp2 in FP64. */
+/* 2^x for the softmax (an approximate, flush-to-zero instruction on the
+ * page's hardware).  The oracle does not imitate an approximate instruction:
+ * it takes exp2 in FP64, rounds once to FP32, and flushes results below the
+ * smallest normal to zero (the page's flush to zero).  Pinned by: numpy exp2
+ * in FP64. */
 float oracle_exp2(float x)
 {
     float r = (float)exp2((double)x);
@@ -114,8 +116,8 @@ float oracle_exp2(float x)
 }
 
 /* Score-domain constant c = (1/sqrt(D)) * log2(e), evaluated in FP64 and
- * rounded once to FP32 ("Attention scale is 1/sqrt(128), converted to base 2",
- * INT8 QK And Score Domain).  Pinned by: the closed form in tests. */
+ * rounded once to FP32 (the page scales scores by 1/sqrt(D) in base 2,
+ * section "INT8 QK And Score Domain").  Pinned by: the closed form in tests. */
 float oracle_score_scale(int D)
 {
     return (float)((1.0 / sqrt((double)D)) * 1.4426950408889634073599246810019);

@@ -134,6 +134,35 @@ def attn_fwd(shape: Shape, bufs: Buffers, o: Optional[torch.Tensor] = None, stre
     return o
 
 
+def attn_segmented_workspace(shape: Shape, nseg: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib.sage_attn_segmented_workspace(ctypes.byref(shape.c()), nseg, ctypes.byref(n)),
+          "sage_attn_segmented_workspace")
+    return n.value
+
+
+def attn_fwd_segmented(shape: Shape, bufs: Buffers, nseg: int, o: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Segmented (split-KV) attention, an opt-in mode that is not the exact
+    order of attn_fwd (sage_attn_fwd_segmented); returns BF16 [B, N, Hq, D]."""
+    if o is None:
+        o = torch.empty((shape.B, shape.N, shape.Hq, shape.D), dtype=torch.bfloat16,
+                        device=bufs.q8.device)
+    if (o.dtype != torch.bfloat16 or o.dim() != 4 or o.shape[0] != shape.B or o.shape[1] < shape.N
+            or o.shape[2] != shape.Hq or o.shape[3] != shape.D or o.device.type != "cuda"):
+        raise ValueError("o must be a BF16 [B, >=N, Hq, D] tensor on the GPU")
+    sb, sn, sh, sd = o.stride()
+    if sd != 1:
+        raise ValueError("o must have unit stride in d")
+    need = attn_segmented_workspace(shape, nseg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
+    check(lib.sage_attn_fwd_segmented(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), nseg, o.data_ptr(),
+                                      sb, sn, sh, workspace.data_ptr(), workspace.numel(), _stream(stream)),
+          "sage_attn_fwd_segmented")
+    return o
+
+
 def forward(q, k, v, w_q=None, w_k=None, cos=None, sin=None, rope_dim: int = 0,
             hadamard: bool = False, eps: float = 1e-5, stream=None):
     """All three passes; returns (o, shape, bufs)."""

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libsage_amd.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m quantized_exact_order_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python quantized_exact_order_amd/build.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -62,6 +62,10 @@ for _name in ("sage_prep", "sage_quant_qk"):
     fn.restype = i32
 _lib.sage_attn_fwd.argtypes = [P(SageShape), P(SageBufs), vp, i64, i64, i64, vp]
 _lib.sage_attn_fwd.restype = i32
+_lib.sage_attn_segmented_workspace.argtypes = [P(SageShape), i32, P(sz)]
+_lib.sage_attn_segmented_workspace.restype = i32
+_lib.sage_attn_fwd_segmented.argtypes = [P(SageShape), P(SageBufs), i32, vp, i64, i64, i64, vp, sz, vp]
+_lib.sage_attn_fwd_segmented.restype = i32
 _lib.sage_kv_append.argtypes = [P(SageKvCache), P(SageView), P(SageView), i32, i32, vp]
 _lib.sage_kv_append.restype = i32
 _lib.sage_decode_workspace.argtypes = [P(SageKvCache), i32, i32, P(sz)]
@@ -75,6 +79,7 @@ _lib.sage_status_str.restype = ctypes.c_char_p
 _lib.sage_version.restype = i32
 
 EXPORTS = ("sage_buffer_sizes", "sage_prep", "sage_quant_qk", "sage_attn_fwd",
+           "sage_attn_segmented_workspace", "sage_attn_fwd_segmented",
            "sage_kv_append", "sage_decode_workspace", "sage_decode_attn",
            "sage_v8_key_of_slot", "sage_status_str", "sage_version")
 

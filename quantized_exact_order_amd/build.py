@@ -1,6 +1,7 @@
 """Build libsage_amd.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m quantized_exact_order_amd.build
+Usage: python quantized_exact_order_amd/build.py   (a plain script: it does not import the
+package, which needs the library it builds)
 """
 from __future__ import annotations
 

@@ -139,8 +139,12 @@ sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, cons
     return sage_launch_quant(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
 }
 
-sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
-                          int64_t osn, int64_t osh, void *stream) {
+namespace {
+
+// Validates the arguments shared by the attention entry points and fills
+// the kernel parameters (nseg = 1, no partials).
+sage_status build_attn(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb, int64_t osn,
+                       int64_t osh, sage::AttnParams *p) {
     sage_status st = check_shape(shape);
     if (st != SAGE_OK) return st;
     if ((st = check_bufs(bufs)) != SAGE_OK) return st;
@@ -149,18 +153,72 @@ sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *
     if (!aligned16(o) || (osb & 7)) return SAGE_E_ALIGN;
     sage_sizes z;
     fill_sizes(shape, &z);
+    std::memset(p, 0, sizeof(*p));
+    p->B = shape->B; p->N = shape->N; p->Hq = shape->Hq; p->Hkv = shape->Hkv;
+    p->grp = shape->Hq / shape->Hkv;
+    p->nq = (int)z.n_q_groups; p->nk = (int)z.n_k_tiles;
+    p->q_rows = z.q_rows; p->k_rows = z.k_rows;
+    p->c = (float)((1.0 / std::sqrt((double)shape->D)) * 1.4426950408889634073599246810019);
+    p->q8 = bufs->q8; p->q_scale = bufs->q_scale; p->k8 = bufs->k8; p->k_scale = bufs->k_scale;
+    p->v8 = bufs->v8; p->v_scale = bufs->v_scale;
+    p->o = static_cast<uint16_t *>(o);
+    p->osb = osb; p->osn = osn; p->osh = osh;
+    p->nseg = 1;
+    return SAGE_OK;
+}
+
+// Bytes of the segment partials: RO [B, Hq, nseg, N, D] FP32, then (m, d)
+// [B, Hq, nseg, N, 2] FP32 at a 256-byte boundary; 0 if it overflows.
+size_t seg_ro_bytes(const sage_shape *s, int32_t nseg) {
+    const double rows = (double)s->B * s->Hq * nseg * s->N;
+    if (rows * s->D * 4 > 9.0e18) return 0;
+    return round256((size_t)s->B * s->Hq * nseg * s->N * s->D * 4);
+}
+
+sage_status check_nseg(const sage_shape *shape, int32_t nseg) {
+    sage_sizes z;
+    fill_sizes(shape, &z);
+    if (nseg < 1 || nseg > z.n_k_tiles) return SAGE_E_SHAPE;
+    const int64_t nqt = (shape->N + 127) / 128;                    // 128 query rows per work-group
+    if (nqt * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
+    if (seg_ro_bytes(shape, nseg) == 0) return SAGE_E_SHAPE;
+    return SAGE_OK;
+}
+
+}  // namespace
+
+sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
+                          int64_t osn, int64_t osh, void *stream) {
     sage::AttnParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.B = shape->B; p.N = shape->N; p.Hq = shape->Hq; p.Hkv = shape->Hkv;
-    p.grp = shape->Hq / shape->Hkv;
-    p.nq = (int)z.n_q_groups; p.nk = (int)z.n_k_tiles;
-    p.q_rows = z.q_rows; p.k_rows = z.k_rows;
-    p.c = (float)((1.0 / std::sqrt((double)shape->D)) * 1.4426950408889634073599246810019);
-    p.q8 = bufs->q8; p.q_scale = bufs->q_scale; p.k8 = bufs->k8; p.k_scale = bufs->k_scale;
-    p.v8 = bufs->v8; p.v_scale = bufs->v_scale;
-    p.o = static_cast<uint16_t *>(o);
-    p.osb = osb; p.osn = osn; p.osh = osh;
+    sage_status st = build_attn(shape, bufs, o, osb, osn, osh, &p);
+    if (st != SAGE_OK) return st;
     return sage_launch_attn(p, shape->D, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+sage_status sage_attn_segmented_workspace(const sage_shape *shape, int32_t nseg, size_t *bytes) {
+    sage_status st = check_shape(shape);
+    if (st != SAGE_OK) return st;
+    if (!bytes) return SAGE_E_NULL;
+    if ((st = check_nseg(shape, nseg)) != SAGE_OK) return st;
+    *bytes = seg_ro_bytes(shape, nseg) + round256((size_t)shape->B * shape->Hq * nseg * shape->N * 2 * 4);
+    return SAGE_OK;
+}
+
+sage_status sage_attn_fwd_segmented(const sage_shape *shape, const sage_bufs *bufs, int32_t nseg, void *o,
+                                    int64_t osb, int64_t osn, int64_t osh, void *workspace, size_t ws_bytes,
+                                    void *stream) {
+    sage::AttnParams p;
+    sage_status st = build_attn(shape, bufs, o, osb, osn, osh, &p);
+    if (st != SAGE_OK) return st;
+    size_t need = 0;
+    if ((st = sage_attn_segmented_workspace(shape, nseg, &need)) != SAGE_OK) return st;
+    if (!workspace || ws_bytes < need) return SAGE_E_WORKSPACE;
+    if (!aligned16(workspace)) return SAGE_E_ALIGN;
+    p.nseg = nseg;
+    p.seg_ro = static_cast<float *>(workspace);
+    p.seg_md = reinterpret_cast<float *>(static_cast<char *>(workspace) + seg_ro_bytes(shape, nseg));
+    return sage_launch_attn_segmented(p, shape->D, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK
+                                                                                                  : SAGE_E_HIP;
 }
 
 namespace {

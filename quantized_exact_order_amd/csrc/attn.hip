@@ -178,7 +178,39 @@ __device__ __forceinline__ void stage_store_v(const v4i (&src)[CH], uint8_t *vb,
     }
 }
 
-template <int D, int WAVES>
+// Segmented (split-KV) schedule, an opt-in mode outside the contract's
+// exact order: the work-group of segment seg runs only the key tiles
+// [seg nk / nseg, (seg + 1) nk / nseg), from the initial state, and keeps its
+// FP32 partials instead of finalizing.  seg_tiles moves the tile bases to the
+// segment's first tile; the segment's last tile is partial only if it is the
+// sequence's last one.
+__device__ __forceinline__ void seg_tiles(const AttnParams &p, int seg, int nseg, int kt_bytes, const uint8_t *&kbase,
+                                          const uint8_t *&vbase, const float *&ksc, int &nk, int &tail_valid) {
+    const int t0 = (int)((int64_t)seg * p.nk / nseg), t1 = (int)((int64_t)(seg + 1) * p.nk / nseg);
+    kbase += (int64_t)t0 * kt_bytes;
+    vbase += (int64_t)t0 * kt_bytes;
+    ksc += t0;
+    nk = t1 - t0;
+    if (t1 < p.nk) tail_valid = 64;
+}
+
+// A segment's partial for query row n: the lane's RO values (channels
+// 32 blk + 8 r4 + 4 hi + 0..3), and the row's m and d from the lanes of half 0.
+template <int D>
+__device__ __forceinline__ void store_seg_partial(const AttnParams &p, int b, int h, int seg, int nseg, int n, int hi,
+                                                  const v16f (&acc)[D / 32], float m, float d) {
+    const int64_t row = (((int64_t)b * p.Hq + h) * nseg + seg) * p.N + n;
+    float *ro = p.seg_ro + row * D;
+#pragma unroll
+    for (int blk = 0; blk < D / 32; ++blk)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4 *>(ro + 32 * blk + 8 * r4 + 4 * hi) =
+                make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
+    if (hi == 0) *reinterpret_cast<float2 *>(p.seg_md + 2 * row) = make_float2(m, d);
+}
+
+template <int D, int WAVES, bool SEG>
 __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnParams p) {
     constexpr int THREADS = 64 * WAVES;
     constexpr int QTILE = 32 * WAVES;                // query rows per work-group
@@ -199,7 +231,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
     const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
     const int lid = x * xq + min(x, xr) + k;
     const int nqt = (p.N + QTILE - 1) / QTILE;
-    const int qt = lid % nqt, h = (lid / nqt) % p.Hq, b = lid / (nqt * p.Hq);
+    const int nseg = SEG ? p.nseg : 1;
+    const int qt = lid % nqt, seg = (lid / nqt) % nseg;
+    const int h = (lid / (nqt * nseg)) % p.Hq, b = lid / (nqt * nseg * p.Hq);
     const int hk = h / p.grp;
     const int q0 = qt * QTILE + 32 * wave;           // first query row of the wave
     const int g = q0 >> 5;                           // its Q scale group
@@ -215,8 +249,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
     const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
     const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
-    const int nk = p.nk;
-    const int tail_valid = p.N - 64 * (nk - 1);      // valid keys of the last tile (1..64)
+    int nk = p.nk;
+    int tail_valid = p.N - 64 * (nk - 1);            // valid keys of the last tile (1..64)
+    if constexpr (SEG) seg_tiles(p, seg, nseg, KT, kbase, vbase, ksc, nk, tail_valid);
 
     v4i stk[CH], stv[CH];
     auto tile_src = [&](const uint8_t *base, int t) { return base + (int64_t)min(t, nk - 1) * KT; };
@@ -263,8 +298,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
 
     // ---- finalize: d over both lane halves, O = bf16((RO * (1/d)) * v_scale)
     const float dt = dsum + shfl_xor_f(dsum, 32);
-    const float rinv = 1.0f / dt;
     const int n = q0 + col;
+    if constexpr (SEG) {
+        if (n < p.N) store_seg_partial<D>(p, b, h, seg, nseg, n, hi, acc, m, dt);
+        return;
+    }
+    const float rinv = 1.0f / dt;
     if (n < p.N) {
         uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
         const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
@@ -479,7 +518,7 @@ __device__ __forceinline__ void ilv_step(const v16i &sc0, const v16i &sc1, v16i 
     }
 }
 
-template <int D>
+template <int D, bool SEG>
 __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     constexpr int QTILE = 128;
     constexpr int KS = D / 32;
@@ -495,7 +534,9 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
     const int lid = x * xq + min(x, xr) + k;
     const int nqt = (p.N + QTILE - 1) / QTILE;
-    const int qt = lid % nqt, h = (lid / nqt) % p.Hq, b = lid / (nqt * p.Hq);
+    const int nseg = SEG ? p.nseg : 1;
+    const int qt = lid % nqt, seg = (lid / nqt) % nseg;
+    const int h = (lid / (nqt * nseg)) % p.Hq, b = lid / (nqt * nseg * p.Hq);
     const int hk = h / p.grp;
     const int q0 = qt * QTILE + 32 * wave;
     const int g = q0 >> 5;
@@ -510,8 +551,9 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
     const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
     const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
-    const int nk = p.nk;
-    const int tail_valid = p.N - 64 * (nk - 1);     // valid keys of the last tile (1..64)
+    int nk = p.nk;
+    int tail_valid = p.N - 64 * (nk - 1);           // valid keys of the last tile (1..64)
+    if constexpr (SEG) seg_tiles(p, seg, nseg, KT, kbase, vbase, ksc, nk, tail_valid);
 
     v16f acc[KS];
 #pragma unroll
@@ -635,8 +677,12 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     }
 
     const float dt = dsum + shfl_xor_f(dsum, 32);
-    const float rinv = 1.0f / dt;
     const int n = q0 + col;
+    if constexpr (SEG) {
+        if (n < p.N) store_seg_partial<D>(p, b, h, seg, nseg, n, hi, acc, m, dt);
+        return;
+    }
+    const float rinv = 1.0f / dt;
     if (n < p.N) {
         uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
         const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
@@ -656,17 +702,69 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     }
 }
 
+// Combines the segment partials of one output row (segmented schedule):
+// M = max_s m_s, a_s = exp2(m_s - M), d = sum_s d_s a_s and RO = sum_s RO_s a_s
+// (from 0, in increasing s), then O = bf16((RO * (1/d)) * v_scale) as in the
+// exact epilogue; with one segment a_0 = 1 and the result is the exact one.
+// Thread: 4 channels of one row.  Grid (ceil(N / rows per block), Hq, B).
+template <int D>
+__global__ __launch_bounds__(256) void attn_seg_combine_kernel(const AttnParams p) {
+    constexpr int TPR = D / 4, RPB = 256 / TPR;      // threads per row, rows per block
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x * RPB + tid / TPR, d0 = 4 * (tid % TPR);
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (n >= p.N) return;
+    const int hk = h / p.grp;
+    const int64_t row0 = ((int64_t)b * p.Hq + h) * p.nseg * p.N + n;   // segment s: row0 + s * N
+    float M = -INFINITY;
+    for (int s = 0; s < p.nseg; ++s) M = __builtin_fmaxf(M, p.seg_md[2 * (row0 + (int64_t)s * p.N)]);
+    float d = 0.0f, r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+    for (int s = 0; s < p.nseg; ++s) {
+        const int64_t row = row0 + (int64_t)s * p.N;
+        const float2 md = *reinterpret_cast<const float2 *>(p.seg_md + 2 * row);
+        const float4 ro = *reinterpret_cast<const float4 *>(p.seg_ro + row * D + d0);
+        const float a = __builtin_amdgcn_exp2f(md.x - M);
+        d = d + md.y * a;
+        r0 = r0 + ro.x * a;
+        r1 = r1 + ro.y * a;
+        r2 = r2 + ro.z * a;
+        r3 = r3 + ro.w * a;
+    }
+    const float rinv = 1.0f / d;
+    const float4 sc = *reinterpret_cast<const float4 *>(p.v_scale + ((int64_t)b * p.Hkv + hk) * D + d0);
+    uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
+    *reinterpret_cast<uint2 *>(orow + d0) =
+        make_uint2(pack_bf16x2((r0 * rinv) * sc.x, (r1 * rinv) * sc.y), pack_bf16x2((r2 * rinv) * sc.z, (r3 * rinv) * sc.w));
+}
+
 }  // namespace
 }  // namespace sage
 
 hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s) {
     if (D == 128) {
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
-        sage::attn_ilv_kernel<128><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
+        sage::attn_ilv_kernel<128, false><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
         constexpr int W = 4;
         const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
-        sage::attn_wide_kernel<256, W><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
+        sage::attn_wide_kernel<256, W, false><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
     }
+    return hipGetLastError();
+}
+
+hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStream_t s) {
+    if (D == 128) {
+        const unsigned nqt = (unsigned)((p.N + 127) / 128);
+        sage::attn_ilv_kernel<128, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);
+    } else {
+        constexpr int W = 4;
+        const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
+        sage::attn_wide_kernel<256, W, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 64 * W, 0, s>>>(p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned rpb = 256 / (D / 4);
+    if (D == 128) sage::attn_seg_combine_kernel<128><<<dim3((p.N + rpb - 1) / rpb, p.Hq, p.B), 256, 0, s>>>(p);
+    else sage::attn_seg_combine_kernel<256><<<dim3((p.N + rpb - 1) / rpb, p.Hq, p.B), 256, 0, s>>>(p);
     return hipGetLastError();
 }

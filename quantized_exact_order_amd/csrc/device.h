@@ -15,8 +15,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // Number formats.  All conversions that feed a bit-exact output round to
-// nearest-even, as the contract page requires ("round ... to BF16 RN",
-// cvt.rni.sat for INT8, E4M3 RN satfinite).
+// nearest-even, as the contract page requires for BF16, INT8 (saturating) and
+// E4M3 (saturating to the largest finite value).
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
@@ -115,6 +115,11 @@ struct AttnParams {
     const float *v_scale;
     uint16_t *o;
     int64_t osb, osn, osh;
+    // segmented (split-KV) schedule only: nseg runs of key tiles, and the
+    // FP32 partials of each run (RO [B, Hq, nseg, N, D]; m and d [.., N, 2])
+    int nseg;
+    float *seg_ro;
+    float *seg_md;
 };
 
 }  // namespace sage
@@ -123,6 +128,7 @@ struct AttnParams {
 hipError_t sage_launch_prep_stats(const sage::PrepParams &p, hipStream_t s);
 hipError_t sage_launch_quant(const sage::PrepParams &p, hipStream_t s);
 hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s);
+hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStream_t s);
 
 // In-tile key order of a v8 tile row: slot -> key (both 0..63).
 __host__ __device__ __forceinline__ int sage_v8_slot_key(int slot) {

@@ -124,6 +124,32 @@ def test_attn_refusals_happen_before_launch(sage):
     assert call(A, 0, 512, 128, SageBufs(A, 0, A, A, A, A, A)) == "SAGE_E_NULL"
 
 
+def test_segmented_refusals_happen_before_launch(sage):
+    from quantized_exact_order_amd._lib import lib, SageBufs, STATUS_NAMES
+    A = 0x100000
+    shape = sage.Shape(1, 100, 4, 2, 128, 96)                   # 2 key tiles
+    bufs = SageBufs(A, A, A, A, A, A, A)
+    n = ctypes.c_size_t()
+    ws = lambda nseg, s=shape: STATUS_NAMES[lib.sage_attn_segmented_workspace(
+        ctypes.byref(s.c()), nseg, ctypes.byref(n))]
+    assert ws(0) == "SAGE_E_SHAPE" and ws(3) == "SAGE_E_SHAPE"
+    assert ws(2) == "SAGE_OK"
+    r256 = lambda x: x + (-x % 256)
+    assert n.value == r256(1 * 4 * 2 * 100 * 128 * 4) + r256(1 * 4 * 2 * 100 * 2 * 4)   # RO, then (m, d)
+    assert ws(1, sage.Shape(1, 100, 4, 3, 128, 96)) == "SAGE_E_GQA"
+    call = lambda nseg, wsp=A, wsb=1 << 30, o=A: STATUS_NAMES[lib.sage_attn_fwd_segmented(
+        ctypes.byref(shape.c()), ctypes.byref(bufs), nseg, o, 0, 512, 128, wsp, wsb, None)]
+    assert call(2, o=None) == "SAGE_E_NULL"
+    assert call(0) == "SAGE_E_SHAPE" and call(3) == "SAGE_E_SHAPE"
+    assert call(2, wsb=16) == "SAGE_E_WORKSPACE"
+    assert call(2, wsp=None) == "SAGE_E_WORKSPACE"
+    assert call(2, wsp=A + 8) == "SAGE_E_ALIGN"
+    # the grid limit counts the segments: ceil(N/128) * Hq = 16384 * 65535 work-groups per
+    # segment, so 2 segments (2,147,450,880) fit under 2^31 - 1 and 3 do not
+    big = sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96)
+    assert ws(2, big) == "SAGE_OK" and ws(3, big) == "SAGE_E_SHAPE"
+
+
 def test_largest_grid_is_accepted(sage):
     # 2^31 - 1 work-groups is the limit; just under it is accepted
     z = sage.buffer_sizes(sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96))

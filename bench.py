@@ -396,7 +396,7 @@ def main():
                    "B": B, "N": N, "H": Hq, "D": D, "step": "sage_prep+sage_quant_qk+sage_attn_fwd"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_ilv_kernel<128>",
+            "kernel": "attn_ilv_kernel<128, false>",
             "achieved": round(achieved, 3),
             "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s",

@@ -36,10 +36,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float round_bf16(float x) { return bf16_lo(pack_bf16x2(x, 0.0f)); }
 
 // FP32 -> INT8: round to nearest even, saturate to [-128, 127], NaN -> 0.
+// v_cvt_i32_f32 itself maps NaN to 0 and saturates out-of-range values, and
+// its input is already an integer here, so one med3 finishes the clamp.
 __device__ __forceinline__ int32_t to_i8(float x) {
-    float r = rintf(x);                        // v_rndne_f32
-    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
-    return (x == x) ? (int32_t)r : 0;
+    const float r = rintf(x);                  // v_rndne_f32
+    int32_t i;
+    asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(r));
+    return min(max(i, -128), 127);
 }
 
 // FP32 -> OCP E4M3 byte, round to nearest even, saturating finite overflow to

@@ -54,10 +54,10 @@ __device__ __forceinline__ uint4 pack8(const float y[8]) {
 }
 
 // RMSNorm of one row held by L consecutive lanes (8 elements each).  Every
-// lane of the wave must call this (lane exchanges).  Result rounded to BF16.
+// lane of the wave must call this (lane exchanges).  Result rounded to BF16
+// and packed (one RNE conversion per element).
 template <int L>
-__device__ __forceinline__ void rmsnorm8(const float x[8], const uint16_t *w, int j, float eps,
-                                         int D, float y[8]) {
+__device__ __forceinline__ uint4 rmsnorm8(const float x[8], const uint16_t *w, int j, float eps, int D) {
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = x[i] * x[i];
@@ -74,12 +74,13 @@ __device__ __forceinline__ void rmsnorm8(const float x[8], const uint16_t *w, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
     }
+    float n2[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float n1 = x[i] * inv;
-        float n2 = n1 * wv[i];
-        y[i] = round_bf16(n2);
+        n2[i] = n1 * wv[i];
     }
+    return pack8(n2);
 }
 
 // Split-half RoPE of the 8 elements [8j, 8j+8) of row `r` whose normalized
@@ -100,17 +101,19 @@ __device__ __forceinline__ void rope8(const uint16_t *yrow, int j, int n, int R,
         const bool lower = d0 < half;
         const int pd = lower ? d0 + half : d0 - half;     // partner block start
         const int cd = lower ? d0 : pd;                   // coefficient index
-        float pv[8], c[8], s[8];
+        // a*c - b*s (lower) and b*c + a*s (upper) are both y*c + partner*s'
+        // with s' = -s for the lower half: the products are exact, so
+        // negating s before the single rounding of the sum changes nothing
+        float pv[8], c[8], s[8], r[8];
         unpack8(*reinterpret_cast<const uint4 *>(yrow + pd), pv);
         unpack8(*reinterpret_cast<const uint4 *>(cos_t + (int64_t)n * half + cd), c);
-        unpack8(*reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd), s);
+        uint4 sw = *reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd);
+        const uint32_t flip = lower ? 0x80008000u : 0u;
+        sw.x ^= flip; sw.y ^= flip; sw.z ^= flip; sw.w ^= flip;
+        unpack8(sw, s);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float r;
-            if (lower) r = y[i] * c[i] - pv[i] * s[i];     // a*c - b*s
-            else r = y[i] * c[i] + pv[i] * s[i];           // b*c + a*s
-            z[i] = round_bf16(r);
-        }
+        for (int i = 0; i < 8; ++i) r[i] = y[i] * c[i] + pv[i] * s[i];
+        unpack8(pack8(r), z);                            // round to BF16 (RNE), as FP32
         return;
     }
 #pragma unroll
@@ -187,10 +190,9 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr, n = t * 64 + r;
-        float x[8], y[8];
+        float x[8];
         unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
-        rmsnorm8<L>(x, p.w_k, j, p.eps, D, y);
-        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = pack8(y);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_k, j, p.eps, D);
     }
     __syncthreads();
 #pragma unroll
@@ -339,10 +341,9 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int r = pass * RPW + rr, n = 32 * g + r;
-        float x[8], y[8];
+        float x[8];
         unpack8(load_row8(p.q, b, n, h, j, n < p.N), x);
-        rmsnorm8<L>(x, p.w_q, j, p.eps, D, y);
-        *reinterpret_cast<uint4 *>(&yb[r * D + 8 * j]) = pack8(y);
+        *reinterpret_cast<uint4 *>(&yb[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_q, j, p.eps, D);
     }
     __syncthreads();
     float u[NP][8];
@@ -395,10 +396,9 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr, n = t * 64 + r;
-        float x[8], y[8];
+        float x[8];
         unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
-        rmsnorm8<L>(x, p.w_k, j, p.eps, D, y);
-        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = pack8(y);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_k, j, p.eps, D);
     }
     __syncthreads();
     const float *mu = p.k_mean + ((int64_t)b * p.Hkv + h) * D + 8 * j;

@@ -116,6 +116,18 @@ def test_batch_two_and_zero_rows():
     _full_check(inp, "batch 2 with zero rows")
 
 
+def test_infinite_element_in_a_query_row():
+    # one +Inf in a Q row: its RMSNorm scale becomes 0, so that element is
+    # Inf * 0 = NaN (as is its RoPE partner) and the rest of the row is 0;
+    # the INT8 conversion sends NaN to 0, so the row quantizes to zeros and
+    # every prep tensor stays byte-identical to the oracle
+    inp = workloads.make_custom(1, 150, 2, 2, 128, 96, seed=700)
+    inp.q[0, 40, 1, 10] = float("inf")
+    ref, shape, bufs, o = _full_check(inp, "Inf in a Q row")
+    assert not ref.q8[0, 1, 40].any()
+    assert torch.isfinite(o.float()).all()
+
+
 @pytest.mark.timeout(600)
 def test_long_sequence_k_mean_tree():
     # 1094 key tiles: the tree over tiles is padded to 2048 leaves, which the

@@ -4,7 +4,8 @@ mode, against the oracle's segmented schedule on the same seeded inputs.
 The oracle's inputs come from its own preparation.  One segment must
 reproduce sage_attn_fwd bit for bit.  Every other segmentation must be
 within max-abs 2e-2 and cosine 0.999 of the oracle, overall and per head.
-It must also leave output rows >= N untouched."""
+It must also leave output rows >= N untouched, and one workspace must serve
+repeated calls with any number of segments."""
 import numpy as np
 import pytest
 import torch
@@ -83,6 +84,26 @@ def test_one_segment_is_the_exact_path_d256():
 def test_segmented_small_and_ragged_lengths(N, nseg):
     inp = workloads.make_inputs(workloads.CONFIGS["tiny"], N=N)
     _check(inp, nseg, f"tiny N={N}")
+
+
+def test_one_workspace_serves_repeated_calls_and_segment_counts():
+    # one workspace gives the same outputs over repeated calls and any nseg
+    import quantized_exact_order_amd as sage
+    inp = workloads.make_inputs(workloads.CONFIGS["tail"])
+    banner("segmented workspace reuse")
+    shape, bufs, _ = run_path(inp, attn=False)
+    need = max(sage.attn_segmented_workspace(shape, n) for n in (2, 3, 16))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = {n: sage.attn_fwd_segmented(shape, bufs, n, workspace=ws).clone() for n in (3, 16, 2)}
+    for _ in range(3):
+        for n in (2, 16, 3):
+            o = sage.attn_fwd_segmented(shape, bufs, n, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), first[n].view(torch.int16)), n
+    fresh = {n: sage.attn_fwd_segmented(shape, bufs, n) for n in (2, 3, 16)}
+    torch.cuda.synchronize()
+    for n in (2, 3, 16):
+        assert torch.equal(fresh[n].view(torch.int16), first[n].view(torch.int16)), n
 
 
 def test_rows_past_n_are_untouched():

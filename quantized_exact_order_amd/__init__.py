@@ -82,6 +82,20 @@ class Buffers:
                         self.k_scale.data_ptr(), self.k_mean.data_ptr(), self.v8.data_ptr(),
                         self.v_scale.data_ptr())
 
+    def check(self, shape: Shape) -> None:
+        """Raise unless these buffers have the sizes sage_buffer_sizes gives for shape."""
+        z = buffer_sizes(shape)
+        B, Hq, Hkv, D = shape.B, shape.Hq, shape.Hkv, shape.D
+        want = {"q8": (B, Hq, z.q_rows, D), "q_scale": (B, Hq, z.n_q_groups),
+                "k8": (B, Hkv, z.k_rows, D), "k_scale": (B, Hkv, z.n_k_tiles), "k_mean": (B, Hkv, D),
+                "v8": (B, Hkv, z.n_k_tiles, D, 64), "v_scale": (B, Hkv, D)}
+        for name, shp in want.items():
+            t = getattr(self, name)
+            if tuple(t.shape) != shp or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"buffer {name} must be a contiguous GPU tensor of shape {shp}")
+        if self.workspace.numel() < z.workspace or self.workspace.device.type != "cuda":
+            raise ValueError(f"workspace must hold at least {z.workspace} bytes on the GPU")
+
 
 def _view(t: torch.Tensor, name: str) -> SageView:
     if t.dtype != torch.bfloat16 or t.dim() != 4 or t.device.type != "cuda":
@@ -90,20 +104,34 @@ def _view(t: torch.Tensor, name: str) -> SageView:
     return SageView(t.data_ptr(), sb, sn, sh, sd)
 
 
-def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
-
-
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream)
 
 
+def _aux(t: Optional[torch.Tensor], name: str, numel: int) -> Optional[int]:
+    """Pointer of an optional BF16 side input (RMSNorm weight, RoPE table),
+    checked here: the C ABI cannot tell a host pointer or a short buffer."""
+    if t is None:
+        return None
+    if t.dtype != torch.bfloat16 or t.device.type != "cuda" or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous BF16 GPU tensor of {numel} elements")
+    return t.data_ptr()
+
+
 def _pass(fn, where, shape, bufs, q, k, v, w_q, w_k, cos, sin, stream):
     qv, kv, vv = _view(q, "q"), _view(k, "k"), _view(v, "v")
+    B, N, Hq, Hkv, D = shape.B, shape.N, shape.Hq, shape.Hkv, shape.D
+    for t, name, h in ((q, "q", Hq), (k, "k", Hkv), (v, "v", Hkv)):
+        if tuple(t.shape) != (B, N, h, D):
+            raise ValueError(f"{name} must have shape {(B, N, h, D)}, got {tuple(t.shape)}")
+    bufs.check(shape)
+    half = shape.rope_dim // 2
+    w_q, w_k = _aux(w_q, "w_q", D), _aux(w_k, "w_k", D)
+    cos, sin = _aux(cos, "cos", N * half), _aux(sin, "sin", N * half)
     check(fn(ctypes.byref(shape.c()), ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
-             _ptr(w_q), _ptr(w_k), _ptr(cos), _ptr(sin), ctypes.byref(bufs.c()),
+             w_q, w_k, cos, sin, ctypes.byref(bufs.c()),
              bufs.workspace.data_ptr(), bufs.workspace.numel(), _stream(stream)), where)
 
 
@@ -120,6 +148,7 @@ def quant_qk(shape: Shape, bufs: Buffers, q, k, v, w_q=None, w_k=None, cos=None,
 
 def attn_fwd(shape: Shape, bufs: Buffers, o: Optional[torch.Tensor] = None, stream=None):
     """Fused attention (sage_attn_fwd); returns BF16 [B, N, Hq, D]."""
+    bufs.check(shape)
     if o is None:
         o = torch.empty((shape.B, shape.N, shape.Hq, shape.D), dtype=torch.bfloat16,
                         device=bufs.q8.device)
@@ -145,6 +174,7 @@ def attn_fwd_segmented(shape: Shape, bufs: Buffers, nseg: int, o: Optional[torch
                        workspace: Optional[torch.Tensor] = None, stream=None):
     """Segmented (split-KV) attention, an opt-in mode that is not the exact
     order of attn_fwd (sage_attn_fwd_segmented); returns BF16 [B, N, Hq, D]."""
+    bufs.check(shape)
     if o is None:
         o = torch.empty((shape.B, shape.N, shape.Hq, shape.D), dtype=torch.bfloat16,
                         device=bufs.q8.device)
@@ -224,6 +254,9 @@ def kv_append(cache: KvCache, k, v, t0: int, stream=None) -> None:
     """Rotate, quantize and store K (BF16 [B, n, Hkv, D]) and copy V at
     positions [t0, t0 + n) (sage_kv_append)."""
     kv, vv = _view(k, "k"), _view(v, "v")
+    B, Hkv, D = cache.k8.shape[0], cache.k8.shape[1], cache.k8.shape[3]
+    if k.shape[0] != B or k.shape[2] != Hkv or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k and v must both have shape [{B}, n, {Hkv}, {D}]")
     check(lib.sage_kv_append(ctypes.byref(cache.c()), ctypes.byref(kv), ctypes.byref(vv), t0,
                              k.shape[1], _stream(stream)), "sage_kv_append")
 
@@ -239,6 +272,8 @@ def decode_attn(cache: KvCache, q, T: int, o: Optional[torch.Tensor] = None,
     """Single-query attention of q (BF16 [B, Hq, D]) over cache positions
     [0, T) (sage_decode_attn); returns BF16 [B, Hq, D]."""
     B, Hq, D = q.shape
+    if B != cache.k8.shape[0] or D != cache.k8.shape[3]:
+        raise ValueError(f"q must have shape [{cache.k8.shape[0]}, Hq, {cache.k8.shape[3]}]")
     if o is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, D) or not o.is_contiguous():

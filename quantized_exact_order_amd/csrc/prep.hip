@@ -31,14 +31,14 @@ namespace {
 constexpr int kThreads = 256;
 
 // Loads 8 consecutive BF16 values (16 bytes) of row (b, n, h) starting at
-// element 8*j; zeros when the row is invalid.
+// element 8*j; zeros when the row is invalid.  The load itself is
+// unconditional (an invalid row reads row 0, which always exists), so the
+// kernels can issue every row load of a work-group before using the first.
 __device__ __forceinline__ uint4 load_row8(const View &v, int b, int n, int h, int j, bool valid) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if (valid) {
-        const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)n * v.sn + (int64_t)h * v.sh + 8 * j;
-        r = *reinterpret_cast<const uint4 *>(p);
-    }
-    return r;
+    const int nn = valid ? n : 0;
+    const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
+    const uint4 r = *reinterpret_cast<const uint4 *>(p);
+    return valid ? r : make_uint4(0, 0, 0, 0);
 }
 
 __device__ __forceinline__ void unpack8(uint4 r, float x[8]) {
@@ -53,11 +53,41 @@ __device__ __forceinline__ uint4 pack8(const float y[8]) {
                       pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
 }
 
+// RMSNorm weights of elements [8j, 8j+8) as FP32 (ones when w is NULL),
+// loaded once per kernel.
+__device__ __forceinline__ void load_w8(const uint16_t *w, int j, float wv[8]) {
+    if (w) {
+        unpack8(*reinterpret_cast<const uint4 *>(w + 8 * j), wv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
+    }
+}
+
+// RoPE coefficients for elements [8j, 8j+8) at position n when R/2 is a
+// multiple of 8, so that 8-element blocks pair up whole: 16 bytes of cos and
+// of sin at the pair's lower block (lanes past R read block 0 and do not use
+// it).  Unconditional loads, so they can be issued with the row loads.
+struct Coef8 {
+    uint4 c, s;
+};
+
+__device__ __forceinline__ Coef8 rope_coef8(const uint16_t *cos_t, const uint16_t *sin_t, int n, int j, int R) {
+    Coef8 k = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    const int half = R >> 1, d0 = 8 * j;
+    if (R > 0 && (half & 7) == 0) {
+        const int cd = d0 < half ? d0 : (d0 < R ? d0 - half : 0);
+        k.c = *reinterpret_cast<const uint4 *>(cos_t + (int64_t)n * half + cd);
+        k.s = *reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd);
+    }
+    return k;
+}
+
 // RMSNorm of one row held by L consecutive lanes (8 elements each).  Every
 // lane of the wave must call this (lane exchanges).  Result rounded to BF16
 // and packed (one RNE conversion per element).
 template <int L>
-__device__ __forceinline__ uint4 rmsnorm8(const float x[8], const uint16_t *w, int j, float eps, int D) {
+__device__ __forceinline__ uint4 rmsnorm8(const float x[8], const float wv[8], float eps, int D) {
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = x[i] * x[i];
@@ -67,13 +97,6 @@ __device__ __forceinline__ uint4 rmsnorm8(const float x[8], const uint16_t *w, i
 #pragma unroll
     for (int m = 1; m < L; m <<= 1) ss = ss + shfl_xor_f(ss, m);
     float inv = 1.0f / sqrtf(ss / (float)D + eps);
-    float wv[8];
-    if (w) {
-        unpack8(*reinterpret_cast<const uint4 *>(w + 8 * j), wv);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
-    }
     float n2[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -84,9 +107,11 @@ __device__ __forceinline__ uint4 rmsnorm8(const float x[8], const uint16_t *w, i
 }
 
 // Split-half RoPE of the 8 elements [8j, 8j+8) of row `r` whose normalized
-// values (BF16) sit in LDS row `yrow`; n is the position.
-__device__ __forceinline__ void rope8(const uint16_t *yrow, int j, int n, int R,
-                                      const uint16_t *cos_t, const uint16_t *sin_t, float z[8]) {
+// values (BF16) sit in LDS row `yrow`; n is the position and k its
+// coefficients from rope_coef8 (used when R/2 is a multiple of 8; other
+// widths load per element).
+__device__ __forceinline__ void rope8(const uint16_t *yrow, int j, int n, int R, const uint16_t *cos_t,
+                                      const uint16_t *sin_t, const Coef8 &k, float z[8]) {
     const int half = R >> 1;
     const int d0 = 8 * j;
     float y[8];
@@ -100,14 +125,13 @@ __device__ __forceinline__ void rope8(const uint16_t *yrow, int j, int n, int R,
         // whole 8-element blocks pair up: block j with block j +- half/8
         const bool lower = d0 < half;
         const int pd = lower ? d0 + half : d0 - half;     // partner block start
-        const int cd = lower ? d0 : pd;                   // coefficient index
         // a*c - b*s (lower) and b*c + a*s (upper) are both y*c + partner*s'
         // with s' = -s for the lower half: the products are exact, so
         // negating s before the single rounding of the sum changes nothing
         float pv[8], c[8], s[8], r[8];
         unpack8(*reinterpret_cast<const uint4 *>(yrow + pd), pv);
-        unpack8(*reinterpret_cast<const uint4 *>(cos_t + (int64_t)n * half + cd), c);
-        uint4 sw = *reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd);
+        unpack8(k.c, c);
+        uint4 sw = k.s;
         const uint32_t flip = lower ? 0x80008000u : 0u;
         sw.x ^= flip; sw.y ^= flip; sw.z ^= flip; sw.w ^= flip;
         unpack8(sw, s);
@@ -187,19 +211,32 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
+    // every global load of the work-group first: K and V rows, RoPE
+    // coefficients, RMSNorm weights
+    uint4 kraw[NPASS], vraw[NPASS];
+    Coef8 cf[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        const int r = pass * RPP + rr, n = t * 64 + r;
+        const int n = t * 64 + pass * RPP + rr;
+        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
+        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
+        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
+    }
+    float wv[8];
+    load_w8(p.w_k, j, wv);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr;
         float x[8];
-        unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
-        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_k, j, p.eps, D);
+        unpack8(kraw[pass], x);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, wv, p.eps, D);
     }
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr, n = t * 64 + r;
         float z[8];
-        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, z);
+        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, cf[pass], z);
         if (n >= p.N) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) z[i] = 0.0f;       // padding leaves are +0
@@ -212,9 +249,8 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
     for (int i = 0; i < 8; ++i) vm[i] = 0.0f;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        const int r = pass * RPP + rr, n = t * 64 + r;
         float x[8];
-        unpack8(load_row8(p.v, b, n, h, j, n < p.N), x);
+        unpack8(vraw[pass], x);                            // invalid rows are zeros
 #pragma unroll
         for (int i = 0; i < 8; ++i) vm[i] = __builtin_fmaxf(vm[i], __builtin_fabsf(x[i]));
     }
@@ -338,12 +374,25 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
     const int g = (blockIdx.x / p.Hq) * 4 + wave;
     uint16_t *yb = ybuf[wave];
 
+    // every row load of the wave first, then the RoPE coefficients (all of
+    // them when they fit in registers, else each at its pass)
+    constexpr bool PRE = NP <= 8;
+    uint4 qraw[NP];
+    Coef8 cf[PRE ? NP : 1];
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
-        const int r = pass * RPW + rr, n = 32 * g + r;
+        const int n = 32 * g + pass * RPW + rr;
+        qraw[pass] = load_row8(p.q, b, n, h, j, n < p.N);
+        if constexpr (PRE) cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
+    }
+    float wv[8];
+    load_w8(p.w_q, j, wv);
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int r = pass * RPW + rr;
         float x[8];
-        unpack8(load_row8(p.q, b, n, h, j, n < p.N), x);
-        *reinterpret_cast<uint4 *>(&yb[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_q, j, p.eps, D);
+        unpack8(qraw[pass], x);
+        *reinterpret_cast<uint4 *>(&yb[r * D + 8 * j]) = rmsnorm8<L>(x, wv, p.eps, D);
     }
     __syncthreads();
     float u[NP][8];
@@ -351,7 +400,9 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int r = pass * RPW + rr, n = 32 * g + r;
-        rope8(&yb[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, u[pass]);
+        const int nc = n < p.N ? n : 0;
+        const Coef8 k = PRE ? cf[PRE ? pass : 0] : rope_coef8(p.cos_t, p.sin_t, nc, j, p.R);
+        rope8(&yb[r * D], j, nc, p.R, p.cos_t, p.sin_t, k, u[pass]);
         if (p.hadamard) wht8<L>(u[pass], j);
         if (n < p.N) {
 #pragma unroll
@@ -393,25 +444,37 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
+    // every global load of the work-group first: K rows, RoPE coefficients,
+    // RMSNorm weights and the K mean
+    uint4 kraw[NPASS];
+    Coef8 cf[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        const int r = pass * RPP + rr, n = t * 64 + r;
-        float x[8];
-        unpack8(load_row8(p.k, b, n, h, j, n < p.N), x);
-        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, p.w_k, j, p.eps, D);
+        const int n = t * 64 + pass * RPP + rr;
+        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
+        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
     }
-    __syncthreads();
+    float wv[8];
+    load_w8(p.w_k, j, wv);
     const float *mu = p.k_mean + ((int64_t)b * p.Hkv + h) * D + 8 * j;
     float mean[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) mean[i] = mu[i];
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int r = pass * RPP + rr;
+        float x[8];
+        unpack8(kraw[pass], x);
+        *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, wv, p.eps, D);
+    }
+    __syncthreads();
     float u[NPASS][8];
     float amax = 0.0f;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr, n = t * 64 + r;
         float z[8];
-        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, z);
+        rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, cf[pass], z);
 #pragma unroll
         for (int i = 0; i < 8; ++i) u[pass][i] = z[i] - mean[i];
         if (p.hadamard) wht8<L>(u[pass], j);
@@ -457,11 +520,15 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
 
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
+    uint4 vraw[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-        const int r = pass * RPP + rr, n = t * 64 + r;
-        *reinterpret_cast<uint4 *>(&vbuf[r * D + 8 * j]) = load_row8(p.v, b, n, h, j, n < p.N);
+        const int n = t * 64 + pass * RPP + rr;
+        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
     }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass)
+        *reinterpret_cast<uint4 *>(&vbuf[(pass * RPP + rr) * D + 8 * j]) = vraw[pass];
     __syncthreads();
     const float *amax = p.ws_vamax + ((int64_t)b * p.Hkv + h) * D;
     uint8_t *dst = p.v8 + (((int64_t)b * p.Hkv + h) * p.nk + t) * (int64_t)D * 64;

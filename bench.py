@@ -65,6 +65,18 @@ def _traffic():
     return rec.get("bytes_per_launch")
 
 
+def _cpu_model():
+    """The host CPU's model name, or None where /proc/cpuinfo does not give it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, cfg, budget_s: float = 12.0, heads=(0, 27, 55)):
     """The oracle, as it stands, on a bounded sample: the full preparation, then
     attention rows of `heads` in batches until about budget_s seconds of
@@ -92,6 +104,7 @@ def cpu_baseline(inp, cfg, budget_s: float = 12.0, heads=(0, 27, 55)):
         "value": round(cfg.attn_ops / t_full / 1e12, 6),
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": (f"full preparation ({t_prep:.1f} s) + attention of {done} query rows of heads "
                    f"{list(heads)} ({t_rows:.1f} s), attention time extrapolated to all "

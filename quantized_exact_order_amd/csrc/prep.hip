@@ -280,21 +280,30 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 // ---------------------------------------------------------------------------
 // Pass 1b: per (b, h, d) the pairwise tree over the tile sums (padded with +0
 // to P = a power of two), mean = S/N; V channel maximum over tiles, floored at
-// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv, D/32), 256 threads: a block
-// owns 32 columns, thread group g (8 of them) the chunks g, g+8, ... of C
+// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv, D/32), 1024 threads: a block
+// owns 32 columns, thread group g (32 of them) the chunks g, g+32 of C
 // consecutive tiles.  The tree over P leaves is the tree over the P/C aligned
 // chunk subtrees, so each thread builds whole chunk subtrees and the block
 // finishes the tree over the (at most 64) chunk sums level by level in LDS.
+// The kernel is latency-bound (34 MB at the canonical size), so it spreads
+// the chunks over 16 waves per block and issues each chunk's loads together.
 // ---------------------------------------------------------------------------
 constexpr int kRedCols = 32;
-constexpr int kRedGroups = 8;
+constexpr int kRedGroups = 32;
+constexpr int kRedThreads = kRedCols * kRedGroups;
 
 // Pairwise tree over the C leaves (C a power of two, at most 16) of tiles
-// t0 .. t0+C-1; tiles >= nk are +0.
+// t0 .. t0+C-1; tiles >= nk are +0.  The loads are unconditional (a leaf past
+// the column reads tile 0, which always exists), so all of them are in flight
+// before the first add.
 __device__ __forceinline__ float chunk_tree16(const float *col, int D, int t0, int C, int nk) {
     float v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = (k < C && t0 + k < nk) ? col[(int64_t)(t0 + k) * D] : 0.0f;
+    for (int k = 0; k < 16; ++k) {
+        const bool in = k < C && t0 + k < nk;
+        const float x = col[(int64_t)(in ? t0 + k : 0) * D];
+        v[k] = in ? x : 0.0f;
+    }
 #pragma unroll
     for (int w = 8; w >= 1; w >>= 1) {
         if (w < C) {
@@ -303,6 +312,21 @@ __device__ __forceinline__ float chunk_tree16(const float *col, int D, int t0, i
         }
     }
     return v[0];
+}
+
+// Maximum of the column over tiles t0 .. min(t0 + C, nk) - 1 (C at most 16),
+// starting from m; every load is issued before the first maximum.
+__device__ __forceinline__ float chunk_max16(const float *col, int D, int t0, int C, int nk, float m) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const bool in = k < C && t0 + k < nk;
+        const float x = col[(int64_t)(in ? t0 + k : 0) * D];     // tile 0 always exists
+        v[k] = in ? x : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, v[k]);
+    return m;
 }
 
 // The same tree for any power of two C: the binary-counter evaluation (after
@@ -320,7 +344,7 @@ __device__ float chunk_tree(const float *col, int D, int t0, int C, int nk) {
     return stack[0];
 }
 
-__global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepParams p) {
+__global__ __launch_bounds__(kRedThreads) void prep_reduce_kernel(const PrepParams p) {
     __shared__ float tree[2][64][kRedCols + 1];
     __shared__ float vmx[kRedGroups][kRedCols];
     const int bh = blockIdx.x, D = p.D, nk = p.nk;
@@ -335,8 +359,7 @@ __global__ __launch_bounds__(256) void prep_reduce_kernel(const PrepParams p) {
     float m = 0.0f;
     for (int j = g; j < NC; j += kRedGroups) {
         tree[0][j][c] = chunk_tree(ks, D, j * C, C, nk);
-        const int te = min((j + 1) * C, nk);
-        for (int t = j * C; t < te; ++t) m = __builtin_fmaxf(m, vm[(int64_t)t * D]);
+        for (int t = j * C; t < (j + 1) * C && t < nk; t += 16) m = chunk_max16(vm, D, t, min(16, (j + 1) * C - t), nk, m);
     }
     vmx[g][c] = m;
     __syncthreads();
@@ -566,7 +589,7 @@ hipError_t sage_launch_prep_stats(const PrepParams &p, hipStream_t s) {
     else sage::prep_stats_kernel<256><<<grid, sage::kThreads, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv, p.D / sage::kRedCols), 256, 0, s>>>(p);
+    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv, p.D / sage::kRedCols), sage::kRedThreads, 0, s>>>(p);
     return hipGetLastError();
 }
 

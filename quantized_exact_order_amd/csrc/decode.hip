@@ -142,13 +142,15 @@ __device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const fl
         const int tok = min(ts + 8 * (r16 >> 2) + 4 * bb + (r16 & 3), T - 1);
         const int8_t *kr = kb + (int64_t)tok * 256 + 16 * q4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) k.a[bb][s] = *reinterpret_cast<const v4i *>(kr + 64 * s);
+        for (int s = 0; s < 4; ++s) k.a[bb][s] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(kr + 64 * s));
     }
     // a group of 8 past T reads the last valid group (its scores are masked);
     // t8 + 8 <= capacity since both are multiples of 8
     const int t8 = min(ts + 8 * q4, ((T - 1) / 8) * 8);
-    k.k0 = *reinterpret_cast<const float4 *>(ksb + t8);
-    k.k1 = *reinterpret_cast<const float4 *>(ksb + t8 + 4);
+    const v4f s0 = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(ksb + t8));
+    const v4f s1 = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(ksb + t8 + 4));
+    k.k0 = make_float4(s0[0], s0[1], s0[2], s0[3]);
+    k.k1 = make_float4(s1[0], s1[1], s1[2], s1[3]);
 }
 
 // The V block of tokens ts + 8 q4 .. + 7 for channels 16 nb + r16 (the B
@@ -158,16 +160,21 @@ __device__ __forceinline__ void load_v_step(uint4 vv[16], const uint16_t *vb, in
     const int blk = min(ts / kVBlock + q4, (T - 1) / kVBlock);
     const uint16_t *vr = vb + ((int64_t)blk * 256 + r16) * kVBlock;
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb) vv[nb] = *reinterpret_cast<const uint4 *>(vr + nb * 16 * kVBlock);
+    for (int nb = 0; nb < 16; ++nb) {
+        const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(vr + nb * 16 * kVBlock));
+        vv[nb] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
 }
 
 // Chunk partial of the grp (<= 16) query heads of one KV head over tokens
 // [128 ns chunk, 128 ns (chunk + 1)).  Grid (nchunk * Hkv, B), 256 threads;
-// wave w streams tokens 128 ns chunk + 32 ns w + [0, 32 ns) in steps of 32
-// with an online softmax (each step's V loads are issued before its K loads,
-// so they are in flight while the scores compute), and the four waves'
-// partials are merged in order.  The query expansion runs while the first
-// step's loads are in flight.
+// step st of wave w covers tokens 128 ns chunk + 128 st + 32 w + [0, 32), so
+// the four waves of a step read adjacent tokens and the work-group streams
+// one contiguous range of the cache.  Each wave runs an online softmax over
+// its steps (each step's V loads are issued before its K loads, so they are
+// in flight while the scores compute), and the four waves' partials are
+// merged in order.  The query expansion runs while the first step's loads are
+// in flight.  The cache is read once: its loads are nontemporal.
 __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int8_t qp[3][kDecodeMaxGroup][kQRow];   // query parts
     __shared__ float qsc[3][kDecodeMaxGroup];                                        // their scales
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     const int64_t bh = (int64_t)b * p.Hkv + hk;
     const int T = p.T;
 
-    const int tw = (chunk * 4 + wave) * 32 * p.ns;
-    const int nst = T > tw ? min((T - tw + 31) / 32, p.ns) : 0;
+    const int tw = chunk * 128 * p.ns + 32 * wave;          // the wave's first token
+    const int nst = T > tw ? min((T - tw + 127) / 128, p.ns) : 0;
     const int8_t *kb = p.k8 + bh * p.cap * 256;
     const float *ksb = p.k_scale + bh * p.cap;
     const uint16_t *vb = p.vc + bh * p.cap * 256;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     for (int nb = 0; nb < 16; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int st = 0; st < nst; ++st) {
-        const int ts = tw + 32 * st;
+        const int ts = tw + 128 * st;
         if (st > 0) {
             load_v_step(vv, vb, ts, T, q4, r16);
             load_k_step(k, kb, ksb, ts, T, q4, r16);

@@ -34,11 +34,13 @@ constexpr int kThreads = 256;
 // element 8*j; zeros when the row is invalid.  The load itself is
 // unconditional (an invalid row reads row 0, which always exists), so the
 // kernels can issue every row load of a work-group before using the first.
+// Each pass streams its rows once, far more bytes than the caches hold, so
+// the load is nontemporal.
 __device__ __forceinline__ uint4 load_row8(const View &v, int b, int n, int h, int j, bool valid) {
     const int nn = valid ? n : 0;
     const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
-    const uint4 r = *reinterpret_cast<const uint4 *>(p);
-    return valid ? r : make_uint4(0, 0, 0, 0);
+    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+    return valid ? make_uint4(x[0], x[1], x[2], x[3]) : make_uint4(0, 0, 0, 0);
 }
 
 __device__ __forceinline__ void unpack8(uint4 r, float x[8]) {

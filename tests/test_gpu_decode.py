@@ -118,6 +118,16 @@ def test_decode_ignores_unwritten_cache_slots(T, cap):
     _check_decode(2, 16, 2, T, cap, seed=70 + T, q_scale=2.0, label="poisoned", poison=True)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,poison", [(4, 8, 4, 8200, True), (4, 16, 4, 20000, False),
+                                                (8, 16, 8, 5000, False)])
+def test_decode_multi_step_chunks(B, Hq, Hkv, T, poison):
+    # caches large enough for several 32-token steps per wave (the waves of a
+    # work-group take interleaved steps), with a last chunk that leaves some
+    # waves fewer steps or none: 8200 = 32 chunks of 256 + 8 tokens,
+    # 20000 = 39 chunks of 512 + 32, 5000 = 9 chunks of 512 + 392
+    _check_decode(B, Hq, Hkv, T, T, seed=80 + B + Hkv, q_scale=2.0, label="multi-step", poison=poison)
+
+
 @pytest.mark.timeout(300)
 def test_decode_long_context():
     _check_decode(1, 16, 4, 32768, 32768, seed=50, q_scale=2.0, label="32k tokens")

@@ -23,6 +23,8 @@
 // of D BF16 values is D/8 lanes), keeps per-row work in registers and uses LDS
 // only for the RoPE partner exchange and the 64-row column reductions.
 
+#include <algorithm>
+
 #include "device.h"
 
 namespace sage {
@@ -282,17 +284,29 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 // ---------------------------------------------------------------------------
 // Pass 1b: per (b, h, d) the pairwise tree over the tile sums (padded with +0
 // to P = a power of two), mean = S/N; V channel maximum over tiles, floored at
-// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv, D/32), 1024 threads: a block
-// owns 32 columns, thread group g (32 of them) the chunks g, g+32 of C
+// 1e-7, and v_scale = amax/2.25.  Grid (B*Hkv, D/32), 32 G threads: a block
+// owns 32 columns, thread group g (G of them) the chunks g, g+G, ... of C
 // consecutive tiles.  The tree over P leaves is the tree over the P/C aligned
 // chunk subtrees, so each thread builds whole chunk subtrees and the block
 // finishes the tree over the (at most 64) chunk sums level by level in LDS.
-// The kernel is latency-bound (34 MB at the canonical size), so it spreads
-// the chunks over 16 waves per block and issues each chunk's loads together.
+// The kernel is latency-bound (34 MB at the canonical size), so the host
+// gives a block one thread group per chunk (G = NC, within 2..32) and each
+// chunk's loads are issued together.
 // ---------------------------------------------------------------------------
 constexpr int kRedCols = 32;
-constexpr int kRedGroups = 32;
-constexpr int kRedThreads = kRedCols * kRedGroups;
+constexpr int kRedMaxGroups = 32;
+
+// Leaves P (nk rounded up to a power of two), tiles per chunk C and chunks NC
+// of the tree over nk tile sums; the same on the host and in the kernel.
+struct RedShape {
+    int P, C, NC;
+};
+__host__ __device__ inline RedShape red_shape(int nk) {
+    int P = 1;
+    while (P < nk) P <<= 1;
+    const int C = (P <= 1024) ? (P < 16 ? P : 16) : P / 64;
+    return RedShape{P, C, P / C};
+}
 
 // Pairwise tree over the C leaves (C a power of two, at most 16) of tiles
 // t0 .. t0+C-1; tiles >= nk are +0.  The loads are unconditional (a leaf past
@@ -346,20 +360,19 @@ __device__ float chunk_tree(const float *col, int D, int t0, int C, int nk) {
     return stack[0];
 }
 
-__global__ __launch_bounds__(kRedThreads) void prep_reduce_kernel(const PrepParams p) {
+__global__ __launch_bounds__(kRedCols * kRedMaxGroups) void prep_reduce_kernel(const PrepParams p) {
     __shared__ float tree[2][64][kRedCols + 1];
-    __shared__ float vmx[kRedGroups][kRedCols];
+    __shared__ float vmx[kRedMaxGroups][kRedCols];
     const int bh = blockIdx.x, D = p.D, nk = p.nk;
+    const int G = blockDim.x / kRedCols;                      // thread groups
     const int c = threadIdx.x % kRedCols, g = threadIdx.x / kRedCols;
     const int d = blockIdx.y * kRedCols + c;
     const float *ks = p.ws_ksum + (int64_t)bh * nk * D + d;
     const float *vm = p.ws_vmax + (int64_t)bh * nk * D + d;
-    int P = 1;
-    while (P < nk) P <<= 1;
-    const int C = (P <= 1024) ? (P < 16 ? P : 16) : P / 64;   // tiles per chunk
-    const int NC = P / C;                                     // chunks, <= 64
+    const RedShape rs = red_shape(nk);
+    const int C = rs.C, NC = rs.NC;                           // tiles per chunk, chunks (<= 64)
     float m = 0.0f;
-    for (int j = g; j < NC; j += kRedGroups) {
+    for (int j = g; j < NC; j += G) {
         tree[0][j][c] = chunk_tree(ks, D, j * C, C, nk);
         for (int t = j * C; t < (j + 1) * C && t < nk; t += 16) m = chunk_max16(vm, D, t, min(16, (j + 1) * C - t), nk, m);
     }
@@ -367,14 +380,13 @@ __global__ __launch_bounds__(kRedThreads) void prep_reduce_kernel(const PrepPara
     __syncthreads();
     int src = 0;
     for (int w = NC / 2; w >= 1; w >>= 1) {           // one tree level: left + right
-        for (int j = g; j < w; j += kRedGroups) tree[src ^ 1][j][c] = tree[src][2 * j][c] + tree[src][2 * j + 1][c];
+        for (int j = g; j < w; j += G) tree[src ^ 1][j][c] = tree[src][2 * j][c] + tree[src][2 * j + 1][c];
         src ^= 1;
         __syncthreads();
     }
     if (g == 0) {
         p.k_mean[(int64_t)bh * D + d] = tree[src][0][c] / (float)p.N;
-#pragma unroll
-        for (int i = 1; i < kRedGroups; ++i) m = __builtin_fmaxf(m, vmx[i][c]);
+        for (int i = 1; i < G; ++i) m = __builtin_fmaxf(m, vmx[i][c]);
         const float amax = (m > 1e-7f) ? m : 1e-7f;
         p.v_scale[(int64_t)bh * D + d] = amax / 2.25f;
         p.ws_vamax[(int64_t)bh * D + d] = amax;
@@ -591,7 +603,8 @@ hipError_t sage_launch_prep_stats(const PrepParams &p, hipStream_t s) {
     else sage::prep_stats_kernel<256><<<grid, sage::kThreads, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv, p.D / sage::kRedCols), sage::kRedThreads, 0, s>>>(p);
+    const int groups = std::min(sage::kRedMaxGroups, std::max(2, sage::red_shape(p.nk).NC));
+    sage::prep_reduce_kernel<<<dim3(p.B * p.Hkv, p.D / sage::kRedCols), sage::kRedCols * groups, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
  * sage.h -- C ABI of the MI355X (gfx950) quantized attention forward.
  *
  * The path computes the SageAttention-style INT8-QK / FP8-PV attention fixed by
- * the page "Exact Numerical Contract" (vortex_exact_attention):
+ * the page "Exact Numerical Contract":
  *   sage_prep      section "Preparation" steps 1-4 (RMSNorm, RoPE, global K
  *                  mean) and the V maximum of section "V And PV";
  *   sage_quant_qk  section "Q And K Quantization" (INT8 Q per 32 rows, INT8 K
@@ -213,11 +213,12 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
  *   s_t = ((H q / 16) . k8_t) * k_scale_t / 16,  w = softmax(s),
  *   o = bf16(sum_t w_t v_t)
  * o: BF16 [B, Hq, D] contiguous.  The cache is read once: the work-group of
- * one KV head and 256 tokens serves its Hq / Hkv query heads on the matrix
- * cores (exact INT32 dot products of K with a three-part INT8 expansion of
- * the rotated query; BF16 V times a two-part BF16 split of the weights, FP32
- * accumulation), and the chunk partials are combined in a fixed order
- * (deterministic).
+ * one KV head and a chunk of 128 * ns tokens (ns in 1..16, set from the cache
+ * size so that the step has about 512 work-groups) serves its Hq / Hkv query
+ * heads on the matrix cores (exact INT32 dot products of K with a three-part
+ * INT8 expansion of the rotated query; BF16 V times a two-part BF16 split of
+ * the weights, FP32 accumulation), and the chunk partials are combined in a
+ * fixed order (deterministic).
  * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256, Hq / Hkv > 16),
  * SAGE_E_GQA, SAGE_E_SHAPE (T < 1 or T > capacity),
  * SAGE_E_STRIDE, SAGE_E_ALIGN, SAGE_E_WORKSPACE, SAGE_E_HIP. */

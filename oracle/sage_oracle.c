@@ -5,7 +5,7 @@
  * call this file: only tests/, the smoke check and the benchmark's CPU
  * baseline use it.  It shares no code, header or table with the HIP library.
  *
- * Authority: the page "Exact Numerical Contract" (vortex_exact_attention),
+ * Authority: the page "Exact Numerical Contract",
  * sections "Preparation", "Q And K Quantization", "INT8 QK And Score Domain",
  * "Online Softmax", "V And PV", "Finalization And Tails".  Where that page is
  * silent the reading used is stated next to the step.  The Walsh-Hadamard

@@ -49,12 +49,13 @@ void fill_sizes(const sage_shape *s, sage_sizes *z) {
     z->workspace = 2 * part + round256((size_t)(B * Hkv * D) * 4);
 }
 
-sage_status check_view(const sage_view_bf16 *v, int H, const sage_shape *s) {
+// A BF16 view: unit d stride, non-negative strides, 16-byte aligned rows.
+// Its extent cannot be checked here; the caller owns that.
+sage_status check_view(const sage_view_bf16 *v) {
     if (!v || !v->ptr) return SAGE_E_NULL;
     if (v->sd != 1) return SAGE_E_STRIDE;
     if (v->sb < 0 || v->sn < 0 || v->sh < 0) return SAGE_E_STRIDE;
     if (!aligned16(v->ptr) || (v->sb & 7) || (v->sn & 7) || (v->sh & 7)) return SAGE_E_ALIGN;
-    (void)H;
     return SAGE_OK;
 }
 
@@ -74,9 +75,9 @@ sage_status build_prep(const sage_shape *shape, const sage_view_bf16 *q, const s
                        void *workspace, size_t ws_bytes, sage::PrepParams *p) {
     sage_status st = check_shape(shape);
     if (st != SAGE_OK) return st;
-    if ((st = check_view(q, shape->Hq, shape)) != SAGE_OK) return st;
-    if ((st = check_view(k, shape->Hkv, shape)) != SAGE_OK) return st;
-    if ((st = check_view(v, shape->Hkv, shape)) != SAGE_OK) return st;
+    if ((st = check_view(q)) != SAGE_OK) return st;
+    if ((st = check_view(k)) != SAGE_OK) return st;
+    if ((st = check_view(v)) != SAGE_OK) return st;
     if ((st = check_bufs(bufs)) != SAGE_OK) return st;
     if (shape->rope_dim > 0 && (!rope_cos || !rope_sin)) return SAGE_E_NULL;
     if (shape->rope_dim > 0 && (shape->rope_dim / 2) % 8 == 0 && (!aligned16(rope_cos) || !aligned16(rope_sin)))
@@ -233,23 +234,14 @@ sage_status check_cache(const sage_kv_cache *c) {
     return SAGE_OK;
 }
 
-sage_status check_view_any(const sage_view_bf16 *v) {
-    if (!v || !v->ptr) return SAGE_E_NULL;
-    if (v->sd != 1) return SAGE_E_STRIDE;
-    if (v->sb < 0 || v->sn < 0 || v->sh < 0) return SAGE_E_STRIDE;
-    if (!aligned16(v->ptr) || (v->sb & 7) || (v->sn & 7) || (v->sh & 7)) return SAGE_E_ALIGN;
-    return SAGE_OK;
-}
-
-
 }  // namespace
 
 sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, const sage_view_bf16 *v,
                            int32_t t0, int32_t n, void *stream) {
     sage_status st = check_cache(cache);
     if (st != SAGE_OK) return st;
-    if ((st = check_view_any(k)) != SAGE_OK) return st;
-    if ((st = check_view_any(v)) != SAGE_OK) return st;
+    if ((st = check_view(k)) != SAGE_OK) return st;
+    if ((st = check_view(v)) != SAGE_OK) return st;
     if (n < 1 || t0 < 0 || (int64_t)t0 + n > cache->capacity) return SAGE_E_SHAPE;
     const int64_t nblk = ((int64_t)t0 + n - 1) / sage::kVBlock - t0 / sage::kVBlock + 1;
     if (nblk * cache->Hkv > 2147483647LL - 3) return SAGE_E_SHAPE;
@@ -276,7 +268,7 @@ sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_
                              void *o, void *workspace, size_t ws_bytes, void *stream) {
     sage_status st = check_cache(cache);
     if (st != SAGE_OK) return st;
-    if ((st = check_view_any(q)) != SAGE_OK) return st;
+    if ((st = check_view(q)) != SAGE_OK) return st;
     if (!o) return SAGE_E_NULL;
     if (!aligned16(o)) return SAGE_E_ALIGN;
     if (Hq < 1 || T < 1 || T > cache->capacity) return SAGE_E_SHAPE;

@@ -28,8 +28,8 @@ from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageKvCache, SageShap
                    SageView, check, lib)
 
 __all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
-           "v8_logical", "v8_slot_keys", "KvCache", "kv_append", "decode_workspace", "decode_attn",
-           "SageError", "LIB_PATH", "EXPORTS"]
+           "attn_segmented_workspace", "attn_fwd_segmented", "v8_logical", "v8_slot_keys", "KvCache",
+           "kv_append", "decode_workspace", "decode_attn", "SageError", "LIB_PATH", "EXPORTS"]
 
 
 @dataclass(frozen=True)
@@ -86,15 +86,16 @@ class Buffers:
         """Raise unless these buffers have the sizes sage_buffer_sizes gives for shape."""
         z = buffer_sizes(shape)
         B, Hq, Hkv, D = shape.B, shape.Hq, shape.Hkv, shape.D
-        want = {"q8": (B, Hq, z.q_rows, D), "q_scale": (B, Hq, z.n_q_groups),
-                "k8": (B, Hkv, z.k_rows, D), "k_scale": (B, Hkv, z.n_k_tiles), "k_mean": (B, Hkv, D),
-                "v8": (B, Hkv, z.n_k_tiles, D, 64), "v_scale": (B, Hkv, D)}
-        for name, shp in want.items():
+        i8, f32, u8 = torch.int8, torch.float32, torch.uint8
+        want = {"q8": ((B, Hq, z.q_rows, D), i8), "q_scale": ((B, Hq, z.n_q_groups), f32),
+                "k8": ((B, Hkv, z.k_rows, D), i8), "k_scale": ((B, Hkv, z.n_k_tiles), f32),
+                "k_mean": ((B, Hkv, D), f32), "v8": ((B, Hkv, z.n_k_tiles, D, 64), u8),
+                "v_scale": ((B, Hkv, D), f32)}
+        for name, (shp, dt) in want.items():
             t = getattr(self, name)
-            if tuple(t.shape) != shp or not t.is_contiguous() or t.device.type != "cuda":
-                raise ValueError(f"buffer {name} must be a contiguous GPU tensor of shape {shp}")
-        if self.workspace.numel() < z.workspace or self.workspace.device.type != "cuda":
-            raise ValueError(f"workspace must hold at least {z.workspace} bytes on the GPU")
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"buffer {name} must be a contiguous {dt} GPU tensor of shape {shp}")
+        _workspace(self.workspace, z.workspace)
 
 
 def _view(t: torch.Tensor, name: str) -> SageView:
@@ -108,6 +109,13 @@ def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream)
+
+
+def _workspace(t: torch.Tensor, need: int) -> None:
+    """A caller's workspace: contiguous GPU bytes, at least `need` of them (the
+    C ABI checks the count it is told, not where the memory is)."""
+    if t.device.type != "cuda" or not t.is_contiguous() or t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous GPU tensor of at least {need} bytes")
 
 
 def _aux(t: Optional[torch.Tensor], name: str, numel: int) -> Optional[int]:
@@ -132,7 +140,8 @@ def _pass(fn, where, shape, bufs, q, k, v, w_q, w_k, cos, sin, stream):
     cos, sin = _aux(cos, "cos", N * half), _aux(sin, "sin", N * half)
     check(fn(ctypes.byref(shape.c()), ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
              w_q, w_k, cos, sin, ctypes.byref(bufs.c()),
-             bufs.workspace.data_ptr(), bufs.workspace.numel(), _stream(stream)), where)
+             bufs.workspace.data_ptr(), bufs.workspace.numel() * bufs.workspace.element_size(),
+             _stream(stream)), where)
 
 
 def prep(shape: Shape, bufs: Buffers, q, k, v, w_q=None, w_k=None, cos=None, sin=None, stream=None):
@@ -185,10 +194,12 @@ def attn_fwd_segmented(shape: Shape, bufs: Buffers, nseg: int, o: Optional[torch
     if sd != 1:
         raise ValueError("o must have unit stride in d")
     need = attn_segmented_workspace(shape, nseg)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
+    _workspace(workspace, need)
     check(lib.sage_attn_fwd_segmented(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), nseg, o.data_ptr(),
-                                      sb, sn, sh, workspace.data_ptr(), workspace.numel(), _stream(stream)),
+                                      sb, sn, sh, workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
           "sage_attn_fwd_segmented")
     return o
 
@@ -245,7 +256,17 @@ class KvCache:
         return self.v.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nb * 8, D)
 
     def c(self) -> SageKvCache:
+        """The C view of the cache, after checking that the three tensors agree:
+        the C ABI takes their pointers and sizes on trust."""
+        if self.k8.dim() != 4:
+            raise ValueError("k8 must be an int8 [B, Hkv, capacity, D] tensor")
         B, Hkv, cap, D = self.k8.shape
+        want = ((self.k8, (B, Hkv, cap, D), torch.int8), (self.k_scale, (B, Hkv, cap), torch.float32),
+                (self.v, (B, Hkv, cap // 8, D, 8), torch.bfloat16))
+        for t, shp, dt in want:
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError(f"cache tensors must be contiguous GPU tensors: k8 int8 [B, Hkv, capacity, D], "
+                                 f"k_scale float32 [B, Hkv, capacity], v bfloat16 [B, Hkv, capacity/8, D, 8]")
         return SageKvCache(self.k8.data_ptr(), self.k_scale.data_ptr(), self.v.data_ptr(),
                            B, Hkv, D, cap)
 
@@ -276,12 +297,18 @@ def decode_attn(cache: KvCache, q, T: int, o: Optional[torch.Tensor] = None,
         raise ValueError(f"q must have shape [{cache.k8.shape[0]}, Hq, {cache.k8.shape[3]}]")
     if o is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
-    if o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, D) or not o.is_contiguous():
-        raise ValueError("o must be a contiguous BF16 [B, Hq, D] tensor")
-    need = decode_workspace(cache, Hq, T)
-    if workspace is None or workspace.numel() < need:
+    if (o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, D) or not o.is_contiguous()
+            or o.device.type != "cuda"):
+        raise ValueError("o must be a contiguous BF16 [B, Hq, D] GPU tensor")
+    cc = cache.c()
+    n = ctypes.c_size_t()
+    check(lib.sage_decode_workspace(ctypes.byref(cc), Hq, T, ctypes.byref(n)), "sage_decode_workspace")
+    need = n.value
+    if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, need)
     qv = _view(q.unsqueeze(1), "q")
-    check(lib.sage_decode_attn(ctypes.byref(cache.c()), Hq, ctypes.byref(qv), T, o.data_ptr(),
-                               workspace.data_ptr(), workspace.numel(), _stream(stream)), "sage_decode_attn")
+    check(lib.sage_decode_attn(ctypes.byref(cc), Hq, ctypes.byref(qv), T, o.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "sage_decode_attn")
     return o

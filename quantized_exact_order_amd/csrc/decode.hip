@@ -9,9 +9,10 @@
 // D = 256 (the page's head width; 1/sqrt(256) = 1/16 is exact).
 //
 // Decode reads the cache once: the work-group of (b, KV head, chunk of
-// 128 ns tokens) serves all Hq/Hkv (<= 16) query heads of that KV head, each
-// wave streaming its 32 ns tokens in steps of 32 with an online softmax, and
-// both contractions run on the matrix cores:
+// 128 ns tokens) serves all Hq/Hkv (<= 16) query heads of that KV head; its
+// four waves take interleaved 32-token steps (so the work-group streams one
+// contiguous range), each with an online softmax over its steps, and both
+// contractions run on the matrix cores:
 //   * scores: the rotated query of each head is expanded as
 //     qr = s1 q1 + s2 q2 + s3 q3 + r with INT8 parts q_j, s_{j+1} = s_j / 128
 //     and |r| <= s3 / 2 (below FP32 rounding of qr . k8), so that

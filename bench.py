@@ -42,7 +42,6 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense INT8 / FP8 MFMA (5.0 POP/s)
 METRIC = "attention TFLOPS (4·N²·H·D/t) at N=37810,H=56,D=128; % INT8/FP8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_canonical_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "quantized_exact_order_amd", "csrc", "attn.hip")
 
 
 def _attn_source_hash() -> str:

@@ -41,6 +41,14 @@ def test_config_full(name):
     _full_check(workloads.make_inputs(workloads.CONFIGS[name]), name)
 
 
+@pytest.mark.parametrize("B,N,Hq,Hkv,rope", [(2, 700, 8, 2, 96), (1, 333, 14, 2, 96), (1, 200, 4, 1, 0)])
+def test_gqa_d128(B, N, Hq, Hkv, rope):
+    # grouped query heads on the D = 128 kernels: query head h reads KV head
+    # h / (Hq / Hkv) (groups of 4, 7 and 4, two sequences, one without RoPE)
+    inp = workloads.make_custom(B, N, Hq, Hkv, 128, rope, seed=90 + Hq, outlier_frac=0.01)
+    _full_check(inp, f"gqa d128 {Hq}/{Hkv}")
+
+
 @pytest.mark.parametrize("layer", [0, 13, 26])
 def test_encoder_layer(layer):
     cfg = workloads.CONFIGS["encoder"]

@@ -51,6 +51,11 @@ def test_segmented_encoder_layer(layer, nseg):
     _check(workloads.make_inputs(cfg, layer=layer), nseg, f"encoder layer {layer}")
 
 
+@pytest.mark.parametrize("nseg", [2, 5])
+def test_segmented_gqa_d128(nseg):
+    _check(workloads.make_custom(2, 700, 8, 2, 128, 96, seed=95, outlier_frac=0.01), nseg, "gqa d128 8/2")
+
+
 @pytest.mark.parametrize("nseg", [3, 16])
 def test_segmented_gqa_d256_sampled_rows(nseg):
     cfg = workloads.CONFIGS["gqa"]

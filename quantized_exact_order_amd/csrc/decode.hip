@@ -143,7 +143,7 @@ __device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const fl
         const int tok = min(ts + 8 * (r16 >> 2) + 4 * bb + (r16 & 3), T - 1);
         const int8_t *kr = kb + (int64_t)tok * 256 + 16 * q4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) k.a[bb][s] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(kr + 64 * s));
+        for (int s = 0; s < 4; ++s) k.a[bb][s] = *reinterpret_cast<const v4i *>(kr + 64 * s);
     }
     // a group of 8 past T reads the last valid group (its scores are masked);
     // t8 + 8 <= capacity since both are multiples of 8
@@ -175,7 +175,10 @@ __device__ __forceinline__ void load_v_step(uint4 vv[16], const uint16_t *vb, in
 // its steps (each step's V loads are issued before its K loads, so they are
 // in flight while the scores compute), and the four waves' partials are
 // merged in order.  The query expansion runs while the first step's loads are
-// in flight.  The cache is read once: its loads are nontemporal.
+// in flight.  The cache is read once: the V and scale loads are
+// nontemporal.  The K loads are not: each reads 64 bytes of each of 16 rows
+// (half a cache line per row), and with that shape a nontemporal hint made
+// the step slower (87 against 80 us on the decode workload).
 __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int8_t qp[3][kDecodeMaxGroup][kQRow];   // query parts
     __shared__ float qsc[3][kDecodeMaxGroup];                                        // their scales

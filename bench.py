@@ -21,6 +21,11 @@ HIP graph and replayed, and (c) as one call with the layers stacked along the
 batch dimension (B = 27), which gives the attention launch 27x the
 work-groups of one layer.  All three must produce identical bytes.
 
+--ab OTHER_LIB.so compares the attention launch of another build of the
+library (same ABI) with the in-tree one on the canonical inputs: paired,
+interleaved launches (A B, B A, ...), each timed with HIP events; it prints
+both medians and the median of the paired ratios B/A.
+
 --workload decode times the decode-time INT8 K cache (per-head Hadamard
 rotation, one FP32 scale per (head, token), BF16 V): single-query attention
 of B=4 sequences x 32 query heads over 4 KV heads of D=256 and 32,768 cached
@@ -307,6 +312,72 @@ def run_decode(args):
     print(json.dumps(result), flush=True)
 
 
+def run_ab(args):
+    """Paired, interleaved A/B timing of sage_attn_fwd: the in-tree library (A)
+    against another build of the same ABI (B), on the canonical inputs."""
+    import ctypes
+    import statistics
+    import torch
+    import workloads
+    import quantized_exact_order_amd as sage
+
+    cfg = workloads.CONFIGS["canonical"]
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    buf = inp.qkv.to(dev)
+    Hq, Hkv, D, B, N = cfg.Hq, cfg.Hkv, cfg.D, cfg.B, cfg.N
+    q = buf[:, :, 0:Hq * D].view(B, N, Hq, D)
+    k = buf[:, :, Hq * D:(Hq + Hkv) * D].view(B, N, Hkv, D)
+    v = buf[:, :, (Hq + Hkv) * D:].view(B, N, Hkv, D)
+    w_q, w_k = inp.w_q.to(dev), inp.w_k.to(dev)
+    cos, sin = inp.cos.to(dev).contiguous(), inp.sin.to(dev).contiguous()
+    shape = sage.Shape(B, N, Hq, Hkv, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+    bufs = sage.Buffers.allocate(shape, dev)
+    sage.prep(shape, bufs, q, k, v, w_q, w_k, cos, sin)
+    sage.quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin)
+
+    other = ctypes.CDLL(os.path.abspath(args.ab))
+    other.sage_attn_fwd.argtypes = sage.lib.sage_attn_fwd.argtypes
+    other.sage_attn_fwd.restype = ctypes.c_int32
+    o_a = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    o_b = torch.empty_like(o_a)
+    stream = torch.cuda.current_stream()
+    sb, sn, sh, _ = o_b.stride()
+
+    def launch(which):
+        if which == 0:
+            sage.attn_fwd(shape, bufs, o_a, stream)
+        else:
+            sage.check(other.sage_attn_fwd(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), o_b.data_ptr(),
+                                           sb, sn, sh, ctypes.c_void_p(stream.cuda_stream)), "B sage_attn_fwd")
+
+    for _ in range(max(args.warmup, 1)):
+        launch(0)
+        launch(1)
+    torch.cuda.synchronize()
+    times = [[], []]
+    for i in range(args.pairs):
+        order = (0, 1) if i % 2 == 0 else (1, 0)
+        evs = []
+        for which in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(which)
+            e1.record(stream)
+            evs.append((which, e0, e1))
+        torch.cuda.synchronize()
+        for which, e0, e1 in evs:
+            times[which].append(e0.elapsed_time(e1))
+    ratios = [tb / ta for ta, tb in zip(times[0], times[1])]
+    print(json.dumps({
+        "ab": {"A": sage.LIB_PATH, "B": os.path.abspath(args.ab), "pairs": args.pairs,
+               "median_ms_A": round(statistics.median(times[0]), 4),
+               "median_ms_B": round(statistics.median(times[1]), 4),
+               "median_ratio_B_over_A": round(statistics.median(ratios), 4),
+               "identical_output": bool(torch.equal(o_a.view(torch.int16), o_b.view(torch.int16)))},
+        "config": {"workload": "canonical attention launch, B=1 N=37810 H=56 D=128"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,12 +387,17 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
     ap.add_argument("--workload", choices=("canonical", "encoder", "decode"), default="canonical")
+    ap.add_argument("--ab", metavar="OTHER_LIB", default=None,
+                    help="paired interleaved A/B of sage_attn_fwd against another build of the library")
+    ap.add_argument("--pairs", type=int, default=10, help="A/B pairs (with --ab)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
               "shards by head with no exchange, so one GPU's throughput is the measured figure.",
               file=sys.stderr)
         sys.exit(2)
+    if args.ab:
+        return run_ab(args)
     if args.workload == "encoder":
         return run_encoder(args)
     if args.workload == "decode":

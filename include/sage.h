@@ -225,6 +225,27 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
 sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
                              void *o, void *workspace, size_t ws_bytes, void *stream);
 
+/* Test hook: applies one device number-format primitive of the preparation
+ * kernels, in the exact form they use, to the FP32 values whose bit patterns
+ * are first, first + 1, ..., first + count - 1, and writes the results to out
+ * (device memory, 16-byte aligned), element i for pattern first + i:
+ *   kind 0  BF16, round to nearest even                 uint16 [count]
+ *   kind 1  INT8, round to nearest even, saturate,      int8   [count]
+ *           NaN -> 0
+ *   kind 2  OCP E4M3, round to nearest even, saturate   uint8  [count]
+ *           to +-448, NaN -> 0x7F / 0xFF
+ *   kind 3  RMSNorm reciprocal 1.0f / sqrtf(x)          float  [count]
+ *   kind 4  x / 127.0f (quantization scale)             float  [count]
+ *   kind 5  127.0f / x (quantization multiplier)        float  [count]
+ *   kind 6  x / 2.25f (V scale)                         float  [count]
+ *   kind 7  2.25f / x (V multiplier)                    float  [count]
+ * For tests that compare these roundings with an independent implementation
+ * over every FP32 pattern (Preparation; Q And K Quantization; V And PV).
+ * Refusals: SAGE_E_NULL, SAGE_E_ALIGN, SAGE_E_UNSUPPORTED (kind outside
+ * 0..7), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
+ * SAGE_E_HIP. */
+sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream);
+
 /* Key (0..63, within its tile) stored at position `slot` (0..63) of every
  * channel row of a v8 tile; -1 if slot is out of range. */
 int32_t sage_v8_key_of_slot(int32_t slot);

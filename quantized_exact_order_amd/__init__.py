@@ -29,7 +29,8 @@ from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageKvCache, SageShap
 
 __all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
            "attn_segmented_workspace", "attn_fwd_segmented", "v8_logical", "v8_slot_keys", "KvCache",
-           "kv_append", "decode_workspace", "decode_attn", "SageError", "LIB_PATH", "EXPORTS"]
+           "kv_append", "decode_workspace", "decode_attn", "selftest_primitive", "SageError", "LIB_PATH",
+           "EXPORTS"]
 
 
 @dataclass(frozen=True)
@@ -213,6 +214,24 @@ def forward(q, k, v, w_q=None, w_k=None, cos=None, sin=None, rope_dim: int = 0,
     prep(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
     quant_qk(shape, bufs, q, k, v, w_q, w_k, cos, sin, stream)
     return attn_fwd(shape, bufs, stream=stream), shape, bufs
+
+
+_PRIMITIVE_DTYPES = {0: torch.int16, 1: torch.int8, 2: torch.uint8}
+
+
+def selftest_primitive(kind: int, first: int, count: int, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Test hook (sage_selftest_primitive): device number-format primitive
+    `kind` (0 BF16 bits as int16, 1 INT8, 2 E4M3 bytes, 3..7 FP32 results) of
+    the FP32 values with bit patterns first .. first + count - 1."""
+    dt = _PRIMITIVE_DTYPES.get(kind, torch.float32)
+    if out is None:
+        out = torch.empty(count, dtype=dt, device="cuda")
+    if out.dtype != dt or out.numel() < count or out.device.type != "cuda" or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dt} GPU tensor of at least {count} elements")
+    check(lib.sage_selftest_primitive(kind, first, count, out.data_ptr(), _stream(stream)),
+          "sage_selftest_primitive")
+    return out
 
 
 def v8_slot_keys() -> list:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsage_amd.so")
-SOURCES = ["api.hip", "prep.hip", "attn.hip", "decode.hip"]
+SOURCES = ["api.hip", "prep.hip", "attn.hip", "decode.hip", "selftest.hip"]
 
 # Packed FP32 VALU forms are kept out of the generated code; FMA contraction is
 # off so that every rounding in the bit-exact preparation is the written one.

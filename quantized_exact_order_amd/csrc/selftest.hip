@@ -1,0 +1,45 @@
+// selftest.hip -- test hook for the number-format primitives of device.h.
+//
+// Applies one primitive of the preparation kernels to FP32 inputs given by
+// their bit patterns, so that a test can compare the device rounding with an
+// independent implementation over every pattern.  The primitives are the
+// ones whose results are bit-exact outputs of the preparation (the page
+// "Exact Numerical Contract", sections "Preparation", "Q And K
+// Quantization" and "V And PV"), in the exact form those kernels use:
+//   0  BF16 round to nearest even                          -> uint16
+//   1  INT8 round to nearest even, saturate, NaN -> 0      -> int8
+//   2  OCP E4M3 round to nearest even, saturate to 448     -> uint8
+//   3  RMSNorm reciprocal  1.0f / sqrtf(x)                 -> float
+//   4  quantization scale  x / 127.0f                      -> float
+//   5  quantization multiplier  127.0f / x                 -> float
+//   6  V scale  x / 2.25f                                  -> float
+//   7  V multiplier  2.25f / x                             -> float
+
+#include "device.h"
+
+namespace sage {
+namespace {
+
+__global__ __launch_bounds__(256) void primitive_kernel(int kind, uint32_t first, uint32_t count, void *out) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= count) return;
+    const float x = __uint_as_float(first + i);
+    switch (kind) {
+    case 0: static_cast<uint16_t *>(out)[i] = (uint16_t)(pack_bf16x2(x, 0.0f) & 0xffffu); break;
+    case 1: static_cast<int8_t *>(out)[i] = (int8_t)to_i8(x); break;
+    case 2: static_cast<uint8_t *>(out)[i] = (uint8_t)to_e4m3(x); break;
+    case 3: static_cast<float *>(out)[i] = 1.0f / sqrtf(x); break;
+    case 4: static_cast<float *>(out)[i] = x / 127.0f; break;
+    case 5: static_cast<float *>(out)[i] = 127.0f / x; break;
+    case 6: static_cast<float *>(out)[i] = x / 2.25f; break;
+    default: static_cast<float *>(out)[i] = 2.25f / x; break;
+    }
+}
+
+}  // namespace
+}  // namespace sage
+
+hipError_t sage_launch_primitive(int kind, uint32_t first, uint32_t count, void *out, hipStream_t s) {
+    sage::primitive_kernel<<<dim3((count + 255u) / 256u), 256, 0, s>>>(kind, first, count, out);
+    return hipGetLastError();
+}

@@ -187,3 +187,16 @@ def test_decode_cache_refusals_happen_before_launch(sage):
     assert attn(cache(), 8, 64, wsb=16) == "SAGE_E_WORKSPACE"
     assert attn(cache(), 8, 64, ws=0) == "SAGE_E_WORKSPACE"
     assert attn(cache(), 8, 64, o=A + 8) == "SAGE_E_ALIGN"
+
+
+def test_primitive_hook_refusals_happen_before_launch(sage):
+    from quantized_exact_order_amd._lib import lib, STATUS_NAMES
+    A = 0x100000
+    prim = lambda kind, first, count, out=A: STATUS_NAMES[lib.sage_selftest_primitive(kind, first, count, out, None)]
+    assert prim(0, 0, 16, out=None) == "SAGE_E_NULL"
+    assert prim(0, 0, 16, out=A + 4) == "SAGE_E_ALIGN"
+    assert prim(-1, 0, 16) == "SAGE_E_UNSUPPORTED"
+    assert prim(8, 0, 16) == "SAGE_E_UNSUPPORTED"
+    assert prim(0, 0, 0) == "SAGE_E_SHAPE"
+    assert prim(0, 0, (1 << 26) + 1) == "SAGE_E_SHAPE"             # more than one chunk
+    assert prim(0, 0xFFFFFFF0, 17) == "SAGE_E_SHAPE"                # runs past pattern 2^32 - 1

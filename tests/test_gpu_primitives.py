@@ -1,0 +1,84 @@
+"""Exhaustive check of the device number-format primitives of the preparation
+(sage_selftest_primitive) over FP32 bit patterns, element by element:
+
+- BF16, INT8 and E4M3 rounding over all 2^32 patterns, against the oracle's
+  own conversion routines (the page "Exact Numerical Contract", sections
+  "Preparation", "Q And K Quantization" and "V And PV": round to nearest
+  even; INT8 saturating with NaN -> 0; E4M3 saturating to +-448);
+- the reciprocal square root of RMSNorm and the scale divisions and
+  multipliers, over every non-negative pattern (their inputs are sums of
+  squares and maxima), against numpy's correctly rounded float32 division
+  and square root.
+
+Results must be bit-identical; where both sides give NaN the payloads are not
+compared."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import banner
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 26
+POS_END = 0x7F800001          # patterns [0, POS_END): +0 up to +inf
+
+
+def _reference(kind, x):
+    if kind == 0:
+        return oracle.f32_to_bf16(x).view(np.int16)
+    if kind == 1:
+        return oracle.f32_to_i8(x)
+    if kind == 2:
+        return oracle.f32_to_e4m3(x)
+    with np.errstate(all="ignore"):
+        if kind == 3:
+            return np.float32(1.0) / np.sqrt(x)
+        if kind == 4:
+            return x / np.float32(127.0)
+        if kind == 5:
+            return np.float32(127.0) / x
+        if kind == 6:
+            return x / np.float32(2.25)
+        return np.float32(2.25) / x
+
+
+def _sweep(kind, end):
+    import quantized_exact_order_amd as sage
+    banner(f"primitive {kind}: patterns [0, {end:#x})")
+    t0 = time.time()
+    out = None
+    first = 0
+    while first < end:
+        n = min(CHUNK, end - first)
+        out = sage.selftest_primitive(kind, first, n, out)
+        torch.cuda.synchronize()
+        got = out[:n].cpu().numpy()
+        bits = np.arange(n, dtype=np.uint32) + np.uint32(first)
+        ref = _reference(kind, bits.view(np.float32))
+        if kind >= 3:
+            g, r = got.view(np.uint32), ref.view(np.uint32)
+            bad = (g != r) & ~(np.isnan(got) & np.isnan(ref))
+        else:
+            bad = got != ref
+        if bad.any():
+            i = int(np.flatnonzero(bad)[0])
+            pytest.fail(f"kind {kind}: pattern {int(bits[i]):#010x} gives {got[i]!r} on the GPU, "
+                        f"{ref[i]!r} in the reference ({int(bad.sum())} of {n} in this chunk)")
+        first += n
+    print(f"[gpu] primitive {kind}: {end} patterns identical ({time.time() - t0:.1f} s)", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_format_conversions_over_all_patterns(kind):
+    _sweep(kind, 1 << 32)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind", [3, 4, 5, 6, 7])
+def test_scale_arithmetic_over_non_negative_patterns(kind):
+    _sweep(kind, POS_END)

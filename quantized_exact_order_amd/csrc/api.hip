@@ -9,6 +9,9 @@
 #include <cmath>
 #include <cstring>
 
+// Defined in selftest.hip (the number-format test hook).
+hipError_t sage_launch_primitive(int kind, uint32_t first, uint32_t count, void *out, hipStream_t s);
+
 namespace {
 
 constexpr int64_t kMaxN = int64_t(1) << 24;

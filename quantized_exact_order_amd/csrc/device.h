@@ -132,7 +132,6 @@ hipError_t sage_launch_prep_stats(const sage::PrepParams &p, hipStream_t s);
 hipError_t sage_launch_quant(const sage::PrepParams &p, hipStream_t s);
 hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s);
 hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStream_t s);
-hipError_t sage_launch_primitive(int kind, uint32_t first, uint32_t count, void *out, hipStream_t s);
 
 // In-tile key order of a v8 tile row: slot -> key (both 0..63).
 __host__ __device__ __forceinline__ int sage_v8_slot_key(int slot) {

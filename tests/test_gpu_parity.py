@@ -124,6 +124,36 @@ def test_batch_two_and_zero_rows():
     _full_check(inp, "batch 2 with zero rows")
 
 
+def test_constant_keys_give_uniform_weights():
+    # every K row of head 0 equal and no RoPE: the pairwise K mean is that row
+    # exactly (300 x a BF16 value is exact in FP32), so smoothing leaves
+    # zeros, every key tile quantizes under the 1e-7 floor, all scores of the
+    # head are 0 and each output row is the weighted mean of the V rows with
+    # equal weights
+    inp = workloads.make_custom(1, 300, 2, 2, 128, 0, seed=710)
+    inp.k[:, :, 0] = inp.k[:, :1, 0]
+    ref, shape, bufs, o = _full_check(inp, "constant keys")
+    assert not ref.k8[0, 0, :300].any()
+
+
+def test_matching_query_and_key_rows_give_peaked_weights():
+    # q = k without RoPE: the diagonal score |y|^2 ~ D stands far above the
+    # others, so every row's weights are sharply peaked at its own key
+    inp = workloads.make_custom(1, 400, 2, 2, 128, 0, seed=720)
+    inp.q[:] = inp.k
+    _full_check(inp, "q = k")
+
+
+def test_constant_v():
+    # head 1 has V = -0.5 everywhere (E4M3 code of -2.25 after scaling, exact)
+    # and head 0 one constant channel
+    inp = workloads.make_custom(1, 257, 2, 2, 128, 96, seed=730)
+    inp.v[:, :, 1] = -0.5
+    inp.v[:, :, 0, 5] = 3.0
+    ref, shape, bufs, o = _full_check(inp, "constant V")
+    assert (o[0, :, 1].float() - (-0.5)).abs().max().item() < 2e-2
+
+
 def test_infinite_element_in_a_query_row():
     # one +Inf in a Q row: its RMSNorm scale becomes 0, so that element is
     # Inf * 0 = NaN (as is its RoPE partner) and the rest of the row is 0;

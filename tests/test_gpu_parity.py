@@ -103,6 +103,17 @@ def test_edge_lengths_d256_gqa_hadamard(N):
     _full_check(inp, f"edge d256 N={N}")
 
 
+@pytest.mark.parametrize("N,D", [(1, 128), (64, 128), (129, 128), (1, 256), (100, 256)])
+def test_single_head(N, D):
+    inp = workloads.make_custom(1, N, 1, 1, D, D * 3 // 4, seed=600 + N + D)
+    _full_check(inp, f"one head N={N} D={D}")
+
+
+def test_d256_without_rotation_or_groups():
+    inp = workloads.make_custom(2, 300, 2, 2, 256, 192, seed=650, outlier_frac=0.01)
+    _full_check(inp, "d256 plain")
+
+
 @pytest.mark.parametrize("R", [0, 2, 40, 128])
 def test_rope_dims(R):
     # R/2 not a multiple of 8 takes the per-element RoPE path

@@ -21,7 +21,7 @@ SOURCES = ["api.hip", "prep.hip", "attn.hip", "decode.hip", "selftest.hip"]
 # off so that every rounding in the bit-exact preparation is the written one.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+         "-Wall", "-Wextra", "-Werror", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
 def _hipcc() -> str:

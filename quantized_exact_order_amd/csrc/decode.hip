@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
         const int g = idx >> 8, d = idx & 255;
         p.part[(((int64_t)b * p.Hq + hk * p.grp + g) * p.nchunk + chunk) * kPartStride + d] = osum[g][d];
     }
-    if (threadIdx.x < p.grp) {
+    if ((int)threadIdx.x < p.grp) {
         const int g = threadIdx.x;
         float *dst = p.part + (((int64_t)b * p.Hq + hk * p.grp + g) * p.nchunk + chunk) * kPartStride;
         const float M = __builtin_fmaxf(__builtin_fmaxf(wm[0][g], wm[1][g]), __builtin_fmaxf(wm[2][g], wm[3][g]));

@@ -104,7 +104,7 @@ def _run_pins(src_text: str, workdir: str, first: str) -> int:
     lib = os.path.join(workdir, "libsage_oracle.so")
     with open(src, "w") as f:
         f.write(src_text)
-    oracle.compile_source(src, lib)
+    oracle.compile_source(src, lib, werror=False)
     files = sorted(PIN_FILES, key=lambda p: first not in p)
     env = dict(os.environ, SAGE_ORACLE_LIB_OVERRIDE=lib, OMP_NUM_THREADS="2")
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider", *files]

@@ -270,6 +270,7 @@ def run_decode(args):
     q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
     cache = sage.KvCache.allocate(B, Hkv, T, dev)
     ws = torch.empty(sage.decode_workspace(cache, Hq, T), dtype=torch.uint8, device=dev)
+    _calibration_copy(args, dev)
     o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
 
     def timed(fn, reps):
@@ -310,6 +311,18 @@ def run_decode(args):
                    "GB_per_s": round(append_bytes / (t_append * 1e-3) / 1e9, 1)},
     }
     print(json.dumps(result), flush=True)
+
+
+def _calibration_copy(args, dev):
+    """A plain device copy of known size (reads and writes calib_copy_mib MiB
+    once), to scale the HBM byte counters of a profiled run."""
+    if args.calib_copy_mib:
+        import torch
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
 
 def run_ab(args):
@@ -434,13 +447,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    if args.calib_copy_mib:
-        # a plain copy of known size: reads and writes calib_copy_mib MiB once
-        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(args, dev)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

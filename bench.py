@@ -26,6 +26,10 @@ library (same ABI) with the in-tree one on the canonical inputs: paired,
 interleaved launches (A B, B A, ...), each timed with HIP events; it prints
 both medians and the median of the paired ratios B/A.
 
+--tails times the attention launch on the canonical inputs at N = 37,810 and,
+on the same views cut to N = 37,760 (295 x 128 rows: no partial query or key
+tile), the tail-free launch; the difference is what the tails cost.
+
 --workload decode times the decode-time INT8 K cache (per-head Hadamard
 rotation, one FP32 scale per (head, token), BF16 V): single-query attention
 of B=4 sequences x 32 query heads over 4 KV heads of D=256 and 32,768 cached
@@ -325,6 +329,68 @@ def _calibration_copy(args, dev):
         del src, dst
 
 
+def run_tails(args):
+    """Attention launch time at the canonical N and at the largest tail-free N
+    below it (a multiple of 128 query rows and 64 keys): same inputs, paired
+    and interleaved launches in one run."""
+    import statistics
+    import torch
+    import workloads
+    import quantized_exact_order_amd as sage
+
+    cfg = workloads.CONFIGS["canonical"]
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    buf = inp.qkv.to(dev)
+    Hq, Hkv, D, B, N = cfg.Hq, cfg.Hkv, cfg.D, cfg.B, cfg.N
+    w_q, w_k = inp.w_q.to(dev), inp.w_k.to(dev)
+    cos, sin = inp.cos.to(dev).contiguous(), inp.sin.to(dev).contiguous()
+    n_free = (N // 128) * 128
+    stream = torch.cuda.current_stream()
+    runs = []
+    for n in (N, n_free):
+        q = buf[:, :n, 0:Hq * D].view(B, n, Hq, D)
+        k = buf[:, :n, Hq * D:(Hq + Hkv) * D].view(B, n, Hkv, D)
+        v = buf[:, :n, (Hq + Hkv) * D:].view(B, n, Hkv, D)
+        shape = sage.Shape(B, n, Hq, Hkv, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+        bufs = sage.Buffers.allocate(shape, dev)
+        c, s_ = cos[:n].contiguous(), sin[:n].contiguous()          # RoPE rows of positions 0..n-1
+        sage.prep(shape, bufs, q, k, v, w_q, w_k, c, s_)
+        sage.quant_qk(shape, bufs, q, k, v, w_q, w_k, c, s_)
+        o = torch.empty((B, n, Hq, D), dtype=torch.bfloat16, device=dev)
+        runs.append((shape, bufs, o))
+    for _ in range(max(args.warmup, 1)):
+        for shape, bufs, o in runs:
+            sage.attn_fwd(shape, bufs, o, stream)
+    torch.cuda.synchronize()
+    times = [[], []]
+    for i in range(args.steps):
+        order = (0, 1) if i % 2 == 0 else (1, 0)
+        evs = []
+        for which in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            shape, bufs, o = runs[which]
+            e0.record(stream)
+            sage.attn_fwd(shape, bufs, o, stream)
+            e1.record(stream)
+            evs.append((which, e0, e1))
+        torch.cuda.synchronize()
+        for which, e0, e1 in evs:
+            times[which].append(e0.elapsed_time(e1))
+    t_full, t_free = statistics.median(times[0]), statistics.median(times[1])
+    diffs = [a - b for a, b in zip(times[0], times[1])]
+    print(json.dumps({
+        "tails": {"N": N, "median_launch_ms": round(t_full, 4),
+                  "N_tail_free": n_free, "median_launch_ms_tail_free": round(t_free, 4),
+                  "median_paired_extra_ms": round(statistics.median(diffs), 4),
+                  "extra_work_fraction": round((N * N - n_free * n_free) / (n_free * n_free), 5),
+                  "pairs": args.steps,
+                  "note": "the extra time covers the 50-row query tail, the 50-key tail tile and the 0.26% more "
+                          "query-key pairs at the canonical N"},
+        "config": {"workload": "canonical attention launch, B=1 H=56 D=128, N=37810 against N=37760"}}),
+        flush=True)
+
+
 def run_ab(args):
     """Paired, interleaved A/B timing of sage_attn_fwd: the in-tree library (A)
     against another build of the same ABI (B), on the canonical inputs."""
@@ -403,6 +469,8 @@ def main():
     ap.add_argument("--ab", metavar="OTHER_LIB", default=None,
                     help="paired interleaved A/B of sage_attn_fwd against another build of the library")
     ap.add_argument("--pairs", type=int, default=10, help="A/B pairs (with --ab)")
+    ap.add_argument("--tails", action="store_true",
+                    help="attention launch at the canonical N against the largest tail-free N below it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
@@ -411,6 +479,8 @@ def main():
         sys.exit(2)
     if args.ab:
         return run_ab(args)
+    if args.tails:
+        return run_tails(args)
     if args.workload == "encoder":
         return run_encoder(args)
     if args.workload == "decode":

@@ -239,10 +239,13 @@ sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_
  *   kind 5  127.0f / x (quantization multiplier)        float  [count]
  *   kind 6  x / 2.25f (V scale)                         float  [count]
  *   kind 7  2.25f / x (V multiplier)                    float  [count]
+ *   kind 8  2^x as the attention kernel's softmax       float  [count]
+ *           computes it (v_exp_f32)
  * For tests that compare these roundings with an independent implementation
- * over every FP32 pattern (Preparation; Q And K Quantization; V And PV).
+ * over every FP32 pattern (Preparation; Q And K Quantization; V And PV), and
+ * that measure the accuracy of the softmax exponential (Online Softmax).
  * Refusals: SAGE_E_NULL, SAGE_E_ALIGN, SAGE_E_UNSUPPORTED (kind outside
- * 0..7), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
+ * 0..8), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
  * SAGE_E_HIP. */
 sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream);
 

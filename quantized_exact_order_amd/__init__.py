@@ -222,7 +222,7 @@ _PRIMITIVE_DTYPES = {0: torch.int16, 1: torch.int8, 2: torch.uint8}
 def selftest_primitive(kind: int, first: int, count: int, out: Optional[torch.Tensor] = None,
                        stream=None) -> torch.Tensor:
     """Test hook (sage_selftest_primitive): device number-format primitive
-    `kind` (0 BF16 bits as int16, 1 INT8, 2 E4M3 bytes, 3..7 FP32 results) of
+    `kind` (0 BF16 bits as int16, 1 INT8, 2 E4M3 bytes, 3..8 FP32 results) of
     the FP32 values with bit patterns first .. first + count - 1."""
     dt = _PRIMITIVE_DTYPES.get(kind, torch.float32)
     if out is None:

@@ -14,6 +14,8 @@
 //   5  quantization multiplier  127.0f / x                 -> float
 //   6  V scale  x / 2.25f                                  -> float
 //   7  V multiplier  2.25f / x                             -> float
+//   8  softmax exponential, the attention kernel's v_exp_f32 -> float
+//      (not a bit-exact output: its accuracy is measured, not pinned)
 
 #include "device.h"
 
@@ -32,7 +34,8 @@ __global__ __launch_bounds__(256) void primitive_kernel(int kind, uint32_t first
     case 4: static_cast<float *>(out)[i] = x / 127.0f; break;
     case 5: static_cast<float *>(out)[i] = 127.0f / x; break;
     case 6: static_cast<float *>(out)[i] = x / 2.25f; break;
-    default: static_cast<float *>(out)[i] = 2.25f / x; break;
+    case 7: static_cast<float *>(out)[i] = 2.25f / x; break;
+    default: static_cast<float *>(out)[i] = __builtin_amdgcn_exp2f(x); break;
     }
 }
 

@@ -8,7 +8,9 @@
 - the reciprocal square root of RMSNorm and the scale divisions and
   multipliers, over every non-negative pattern (their inputs are sums of
   squares and maxima), against numpy's correctly rounded float32 division
-  and square root.
+  and square root;
+- the accuracy of the softmax exponential (not a bit-exact output) over every
+  argument from -126 to 8.81, against FP64.
 
 Results must be bit-identical; where both sides give NaN the payloads are not
 compared."""
@@ -82,3 +84,41 @@ def test_format_conversions_over_all_patterns(kind):
 @pytest.mark.parametrize("kind", [3, 4, 5, 6, 7])
 def test_scale_arithmetic_over_non_negative_patterns(kind):
     _sweep(kind, POS_END)
+
+
+def _exp2_ulp_errors(first, end):
+    import quantized_exact_order_amd as sage
+    worst, worst_x, out = 0.0, None, None
+    while first < end:
+        n = min(CHUNK, end - first)
+        out = sage.selftest_primitive(8, first, n, out)
+        torch.cuda.synchronize()
+        got = out[:n].cpu().numpy().astype(np.float64)
+        x = (np.arange(n, dtype=np.uint32) + np.uint32(first)).view(np.float32)
+        exact = np.exp2(x.astype(np.float64))
+        ulp = np.spacing(exact.astype(np.float32)).astype(np.float64)
+        err = np.abs(got - exact) / ulp
+        i = int(np.argmax(err))
+        if err[i] > worst:
+            worst, worst_x = float(err[i]), float(x[i])
+        first += n
+    return worst, worst_x
+
+
+@pytest.mark.timeout(600)
+def test_softmax_exponential_accuracy():
+    # every FP32 argument the softmax can pass down to -126 (below, the results
+    # are subnormal and the oracle flushes them): 2^x from the attention kernel's
+    # own instruction against FP64, in units of the FP32 ulp of the exact value.
+    # The oracle rounds exp2 once (error <= 0.5 ulp); the device stays within
+    # one ulp (measured maximum 0.78), which the tolerance reading of the
+    # attention output rests on
+    banner("softmax exponential: x in [-126, 8.81]")
+    hi = int(np.float32(8.81).view(np.uint32))
+    lo = int(np.float32(-126.0).view(np.uint32))
+    w_pos, x_pos = _exp2_ulp_errors(0, hi + 1)
+    w_neg, x_neg = _exp2_ulp_errors(0x80000000, lo + 1)
+    worst = max(w_pos, w_neg)
+    print(f"[gpu] v_exp_f32: max error {w_pos:.3f} ulp at x = {x_pos!r} (x >= 0), {w_neg:.3f} ulp at "
+          f"x = {x_neg!r} (x < 0)", flush=True)
+    assert worst <= 1.0

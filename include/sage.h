@@ -91,7 +91,13 @@ typedef struct sage_view_bf16 {
  *   v8       OCP E4M3 [B, Hkv, n_k_tiles, D, 64]: tile t, channel d holds the
  *            64 keys of the tile in the order sage_v8_key_of_slot gives; keys
  *            >= N are zero
- *   v_scale  FP32 [B, Hkv, D]                                                  */
+ *   v_scale  FP32 [B, Hkv, D]
+ *   q_prep   optional (NULL = not written) BF16 [B, Hq, N, D]: Q after RMSNorm
+ *            and RoPE ("Preparation" steps 1-3), before any rotation; written
+ *            by sage_quant_qk
+ *   k_prep   optional (NULL = not written) BF16 [B, Hkv, N, D]: K after
+ *            RMSNorm and RoPE, before mean subtraction and rotation; written
+ *            by sage_quant_qk                                                 */
 typedef struct sage_bufs {
     int8_t *q8;
     float *q_scale;
@@ -100,6 +106,8 @@ typedef struct sage_bufs {
     float *k_mean;
     uint8_t *v8;
     float *v_scale;
+    uint16_t *q_prep;
+    uint16_t *k_prep;
 } sage_bufs;
 
 /* Byte sizes of each buffer of sage_bufs and of the workspace, plus the
@@ -131,7 +139,8 @@ sage_status sage_prep(const sage_shape *shape, const sage_view_bf16 *q, const sa
 /* Pass 2 ("Q And K Quantization"; FP8 cast of "V And PV").  Same arguments as
  * sage_prep.  Recomputes RMSNorm + RoPE (+ rotation) bit-identically to pass 1,
  * subtracts k_mean from K, and writes q8, q_scale, k8, k_scale and v8
- * (including zero padding rows). */
+ * (including zero padding rows), and q_prep / k_prep when they are not NULL
+ * (16-byte aligned, else SAGE_E_ALIGN). */
 sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, const sage_view_bf16 *k,
                           const sage_view_bf16 *v, const uint16_t *w_q, const uint16_t *w_k,
                           const uint16_t *rope_cos, const uint16_t *rope_sin, const sage_bufs *bufs,

@@ -66,22 +66,29 @@ class Buffers:
     v8: torch.Tensor         # uint8 [B, Hkv, n_k_tiles, D, 64] (E4M3, keys in slot order)
     v_scale: torch.Tensor    # f32   [B, Hkv, D]
     workspace: torch.Tensor  # uint8 [sizes.workspace]
+    q_prep: Optional[torch.Tensor] = None   # bf16 [B, Hq, N, D] prepared Q (optional)
+    k_prep: Optional[torch.Tensor] = None   # bf16 [B, Hkv, N, D] prepared K (optional)
 
     @classmethod
-    def allocate(cls, shape: Shape, device) -> "Buffers":
+    def allocate(cls, shape: Shape, device, prep_outputs: bool = False) -> "Buffers":
+        """Buffers for shape; prep_outputs also allocates q_prep / k_prep, the
+        BF16 Q and K after RMSNorm and RoPE that sage_quant_qk then writes."""
         z = buffer_sizes(shape)
-        B, Hq, Hkv, D = shape.B, shape.Hq, shape.Hkv, shape.D
+        B, N, Hq, Hkv, D = shape.B, shape.N, shape.Hq, shape.Hkv, shape.D
         e = lambda *s, dt: torch.empty(s, dtype=dt, device=device)
         return cls(e(B, Hq, z.q_rows, D, dt=torch.int8), e(B, Hq, z.n_q_groups, dt=torch.float32),
                    e(B, Hkv, z.k_rows, D, dt=torch.int8), e(B, Hkv, z.n_k_tiles, dt=torch.float32),
                    e(B, Hkv, D, dt=torch.float32),
                    e(B, Hkv, z.n_k_tiles, D, 64, dt=torch.uint8), e(B, Hkv, D, dt=torch.float32),
-                   e(max(int(z.workspace), 1), dt=torch.uint8))
+                   e(max(int(z.workspace), 1), dt=torch.uint8),
+                   e(B, Hq, N, D, dt=torch.bfloat16) if prep_outputs else None,
+                   e(B, Hkv, N, D, dt=torch.bfloat16) if prep_outputs else None)
 
     def c(self) -> SageBufs:
+        ptr = lambda t: None if t is None else t.data_ptr()
         return SageBufs(self.q8.data_ptr(), self.q_scale.data_ptr(), self.k8.data_ptr(),
                         self.k_scale.data_ptr(), self.k_mean.data_ptr(), self.v8.data_ptr(),
-                        self.v_scale.data_ptr())
+                        self.v_scale.data_ptr(), ptr(self.q_prep), ptr(self.k_prep))
 
     def check(self, shape: Shape) -> None:
         """Raise unless these buffers have the sizes sage_buffer_sizes gives for shape."""
@@ -97,6 +104,11 @@ class Buffers:
             if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"buffer {name} must be a contiguous {dt} GPU tensor of shape {shp}")
         _workspace(self.workspace, z.workspace)
+        for name, h in (("q_prep", Hq), ("k_prep", Hkv)):
+            t = getattr(self, name)
+            if t is not None and (tuple(t.shape) != (B, h, shape.N, D) or t.dtype != torch.bfloat16
+                                  or not t.is_contiguous() or t.device.type != "cuda"):
+                raise ValueError(f"{name} must be a contiguous BF16 GPU tensor of shape {(B, h, shape.N, D)}")
 
 
 def _view(t: torch.Tensor, name: str) -> SageView:

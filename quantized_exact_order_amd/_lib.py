@@ -38,7 +38,7 @@ class SageView(ctypes.Structure):
 
 class SageBufs(ctypes.Structure):
     _fields_ = [("q8", vp), ("q_scale", vp), ("k8", vp), ("k_scale", vp), ("k_mean", vp),
-                ("v8", vp), ("v_scale", vp)]
+                ("v8", vp), ("v_scale", vp), ("q_prep", vp), ("k_prep", vp)]
 
 
 class SageSizes(ctypes.Structure):

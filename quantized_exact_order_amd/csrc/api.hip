@@ -82,6 +82,7 @@ sage_status build_prep(const sage_shape *shape, const sage_view_bf16 *q, const s
     if ((st = check_view(k)) != SAGE_OK) return st;
     if ((st = check_view(v)) != SAGE_OK) return st;
     if ((st = check_bufs(bufs)) != SAGE_OK) return st;
+    if ((bufs->q_prep && !aligned16(bufs->q_prep)) || (bufs->k_prep && !aligned16(bufs->k_prep))) return SAGE_E_ALIGN;
     if (shape->rope_dim > 0 && (!rope_cos || !rope_sin)) return SAGE_E_NULL;
     if (shape->rope_dim > 0 && (shape->rope_dim / 2) % 8 == 0 && (!aligned16(rope_cos) || !aligned16(rope_sin)))
         return SAGE_E_ALIGN;
@@ -101,6 +102,7 @@ sage_status build_prep(const sage_shape *shape, const sage_view_bf16 *q, const s
     p->w_q = w_q; p->w_k = w_k; p->cos_t = rope_cos; p->sin_t = rope_sin;
     p->q8 = bufs->q8; p->q_scale = bufs->q_scale; p->k8 = bufs->k8; p->k_scale = bufs->k_scale;
     p->k_mean = bufs->k_mean; p->v8 = bufs->v8; p->v_scale = bufs->v_scale;
+    p->q_prep = bufs->q_prep; p->k_prep = bufs->k_prep;
     const size_t part = round256((size_t)((int64_t)shape->B * shape->Hkv * z.n_k_tiles * shape->D) * 4);
     char *ws = static_cast<char *>(workspace);
     p->ws_ksum = reinterpret_cast<float *>(ws);

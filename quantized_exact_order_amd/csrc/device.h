@@ -102,6 +102,7 @@ struct PrepParams {
     float *ws_ksum;                     // [B, Hkv, nk, D] per-tile K column sums
     float *ws_vmax;                     // [B, Hkv, nk, D] per-tile V column max |v|
     float *ws_vamax;                    // [B, Hkv, D] floored V channel maximum
+    uint16_t *q_prep, *k_prep;          // optional BF16 [B, H, N, D] prepared Q / K
     int64_t q_rows, k_rows;
     int nq, nk;
 };

@@ -440,6 +440,8 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
         const int nc = n < p.N ? n : 0;
         const Coef8 k = PRE ? cf[PRE ? pass : 0] : rope_coef8(p.cos_t, p.sin_t, nc, j, p.R);
         rope8(&yb[r * D], j, nc, p.R, p.cos_t, p.sin_t, k, u[pass]);
+        if (p.q_prep && n < p.N)
+            *reinterpret_cast<uint4 *>(p.q_prep + (((int64_t)b * p.Hq + h) * p.N + n) * D + 8 * j) = pack8(u[pass]);
         if (p.hadamard) wht8<L>(u[pass], j);
         if (n < p.N) {
 #pragma unroll
@@ -512,6 +514,8 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
         const int r = pass * RPP + rr, n = t * 64 + r;
         float z[8];
         rope8(&ybuf[r * D], j, n < p.N ? n : 0, p.R, p.cos_t, p.sin_t, cf[pass], z);
+        if (p.k_prep && n < p.N)
+            *reinterpret_cast<uint4 *>(p.k_prep + (((int64_t)b * p.Hkv + h) * p.N + n) * D + 8 * j) = pack8(z);
 #pragma unroll
         for (int i = 0; i < 8; ++i) u[pass][i] = z[i] - mean[i];
         if (p.hadamard) wht8<L>(u[pass], j);

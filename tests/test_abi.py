@@ -200,3 +200,14 @@ def test_primitive_hook_refusals_happen_before_launch(sage):
     assert prim(0, 0, 0) == "SAGE_E_SHAPE"
     assert prim(0, 0, (1 << 26) + 1) == "SAGE_E_SHAPE"             # more than one chunk
     assert prim(0, 0xFFFFFFF0, 17) == "SAGE_E_SHAPE"                # runs past pattern 2^32 - 1
+
+
+def test_prepared_output_alignment_is_checked_before_launch(sage):
+    from quantized_exact_order_amd._lib import lib, SageBufs, SageShape, SageView, STATUS_NAMES
+    A = 0x100000
+    shape = SageShape(1, 64, 2, 2, 128, 96, 0, 1e-5)
+    view = SageView(A, 0, 2 * 128, 128, 1)
+    bufs = SageBufs(A, A, A, A, A, A, A, A + 2, None)             # q_prep misaligned
+    st = lib.sage_quant_qk(ctypes.byref(shape), ctypes.byref(view), ctypes.byref(view), ctypes.byref(view),
+                           None, None, A, A, ctypes.byref(bufs), A, 1 << 30, None)
+    assert STATUS_NAMES[st] == "SAGE_E_ALIGN"

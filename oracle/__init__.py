@@ -87,6 +87,7 @@ def lib():
         L.oracle_attn_rows_segmented.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, P, i32, P]
         L.oracle_kv_quant.argtypes = [i32, i32, i32, i32, P, i64, i64, i64, P, P]
         L.oracle_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_decode_attn_v8.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_f64_to_f16.restype = f32
         L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = i32
@@ -394,4 +395,23 @@ def decode_attn(q: torch.Tensor, k8: np.ndarray, kscale: np.ndarray, v_cache: np
     w = np.empty((B, Hq, max(T, 1)), np.float64)
     lib().oracle_decode_attn(B, Hq, Hkv, D, T, Tc, _ptr(qb), _ptr(k8), _ptr(kscale), _ptr(v_cache),
                              _ptr(o), _ptr(w))
+    return o, w[:, :, :T]
+
+
+def decode_attn_v8(q: torch.Tensor, k8: np.ndarray, kscale: np.ndarray, v8: np.ndarray, vscale: np.ndarray,
+                   T: int):
+    """decode_attn over a cache whose V rows are stored like K rows (rotated
+    INT8 v8 [B, Hkv, Tc, D], FP32 vscale [B, Hkv, Tc], as kv_quant gives them);
+    the output is rotated back.  Returns (o uint16 BF16 [B, Hq, D], weights
+    float64 [B, Hq, T])."""
+    B, Hq, D = q.shape
+    Hkv, Tc = k8.shape[1], k8.shape[2]
+    qb = np.ascontiguousarray(q.contiguous().view(torch.int16).numpy().view(np.uint16))
+    k8, v8 = np.ascontiguousarray(k8, np.int8), np.ascontiguousarray(v8, np.int8)
+    kscale = np.ascontiguousarray(kscale, np.float32)
+    vscale = np.ascontiguousarray(vscale, np.float32)
+    o = np.empty((B, Hq, D), np.uint16)
+    w = np.empty((B, Hq, max(T, 1)), np.float64)
+    lib().oracle_decode_attn_v8(B, Hq, Hkv, D, T, Tc, _ptr(qb), _ptr(k8), _ptr(kscale), _ptr(v8), _ptr(vscale),
+                                _ptr(o), _ptr(w))
     return o, w[:, :, :T]

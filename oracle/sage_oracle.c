@@ -721,6 +721,57 @@ void oracle_decode_attn(int B, int Hq, int Hkv, int D, int T, int Tc, const uint
         }
 }
 
+/*
+ * The same decode over a cache whose V is stored like K (the NPU issue page
+ * on INT8 KV with per-head Hadamard rotation, part A: a rotated INT8 V needs
+ * the transform applied once more to the output).  Reading taken: V rows are
+ * rotated and quantized exactly as oracle_kv_quant does for K (one FP32 scale
+ * per (head, token)), and since the normalized transform is its own inverse,
+ * the output is that transform of the weighted sum of dequantized rows:
+ *   r[d] = sum_t w_t * vscale[t] * v8[t, d]               (FP64)
+ *   o    = (1/sqrt(D)) H r  (FP64 butterflies);  O = bf16(float(o))
+ * with w the weights of oracle_decode_attn.  v8 [B, Hkv, Tc, D], vscale
+ * [B, Hkv, Tc]; the other arguments as for oracle_decode_attn.
+ * Pinned by: one token gives back the stored row within the quantization
+ * bound, constant V rows give that row for any weights, and the weights equal
+ * those of oracle_decode_attn.
+ */
+void oracle_decode_attn_v8(int B, int Hq, int Hkv, int D, int T, int Tc, const uint16_t *q,
+                           const int8_t *k8, const float *kscale, const int8_t *v8, const float *vscale,
+                           uint16_t *o, double *w)
+{
+    const int grp = Hq / Hkv;
+    double *wt = (double *)malloc(sizeof(double) * (size_t)B * Hq * (T > 0 ? T : 1));
+    uint16_t *unused = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)B * Hq * D);
+    uint16_t *vzero = (uint16_t *)calloc((size_t)B * Hkv * Tc * D, sizeof(uint16_t));
+    oracle_decode_attn(B, Hq, Hkv, D, T, Tc, q, k8, kscale, vzero, unused, wt);
+    free(vzero);
+    free(unused);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hq; h++) {
+            const int64_t base = ((int64_t)b * Hkv + h / grp) * Tc;
+            const double *wr = wt + ((int64_t)b * Hq + h) * T;
+            double *r = (double *)calloc(D, sizeof(double));
+            for (int t = 0; t < T; t++) {
+                const int8_t *vr = v8 + (base + t) * D;
+                for (int d = 0; d < D; d++) r[d] += wr[t] * (double)vscale[base + t] * (double)vr[d];
+            }
+            for (int span = 1; span < D; span *= 2)
+                for (int i = 0; i < D; i += 2 * span)
+                    for (int j = i; j < i + span; j++) {
+                        const double a = r[j], c = r[j + span];
+                        r[j] = a + c;
+                        r[j + span] = a - c;
+                    }
+            for (int d = 0; d < D; d++)
+                o[((int64_t)b * Hq + h) * D + d] = oracle_f32_to_bf16((float)(r[d] / sqrt((double)D)));
+            free(r);
+        }
+    if (w) memcpy(w, wt, sizeof(double) * (size_t)B * Hq * T);
+    free(wt);
+}
+
 /* Number of OpenMP threads the oracle runs with (for reporting). */
 int oracle_num_threads(void)
 {

@@ -29,6 +29,8 @@ void oracle_kv_quant(int B, int T, int H, int D, const uint16_t *k, int64_t sb, 
                      float *kscale);
 void oracle_decode_attn(int B, int Hq, int Hkv, int D, int T, int Tc, const uint16_t *q, const int8_t *k8,
                         const float *kscale, const uint16_t *v, uint16_t *o, double *w);
+void oracle_decode_attn_v8(int B, int Hq, int Hkv, int D, int T, int Tc, const uint16_t *q, const int8_t *k8,
+                           const float *kscale, const int8_t *v8, const float *vscale, uint16_t *o, double *w);
 
 static uint64_t rng = 0x9E3779B97F4A7C15ull;
 
@@ -91,14 +93,19 @@ static void decode(int B, int Hq, int Hkv, int Tc)
     int8_t *k8 = malloc((size_t)B * Hkv * Tc * D);
     float *ks = malloc((size_t)B * Hkv * Tc * 4);
     oracle_kv_quant(B, Tc, Hkv, D, k, (int64_t)Tc * Hkv * D, (int64_t)Hkv * D, D, k8, ks);
+    int8_t *v8 = malloc((size_t)B * Hkv * Tc * D);
+    float *vs = malloc((size_t)B * Hkv * Tc * 4);
+    /* the V cache [B, Hkv, Tc, D] read as rows [B, T, H, D] with strides */
+    oracle_kv_quant(B, Tc, Hkv, D, vc, (int64_t)Hkv * Tc * D, D, (int64_t)Tc * D, v8, vs);
     uint16_t *o = malloc((size_t)B * Hq * D * 2);
     const int Ts[3] = {1, Tc / 2 + 1, Tc};
     for (int i = 0; i < 3; i++) {
         double *w = malloc((size_t)B * Hq * Ts[i] * sizeof(double));
         oracle_decode_attn(B, Hq, Hkv, D, Ts[i], Tc, q, k8, ks, vc, o, w);
+        oracle_decode_attn_v8(B, Hq, Hkv, D, Ts[i], Tc, q, k8, ks, v8, vs, o, w);
         free(w);
     }
-    free(k); free(vc); free(q); free(k8); free(ks); free(o);
+    free(k); free(vc); free(q); free(k8); free(ks); free(v8); free(vs); free(o);
 }
 
 int main(void)

@@ -143,3 +143,63 @@ def test_kld_gate_rotated_int8_cache(mult):
         assert 0.3 < unrot / rot < 3.0                   # rotation is worth nothing on the control
     if mult == 30:
         assert unrot > 5 * rot and unrot > 1e-3           # and is what keeps x30 inside the gate
+
+
+def _v8_case(rng, B, T, Hq, Hkv, vmul=1.0):
+    q = _bf16(rng.standard_normal((B, Hq, D)) * 2.0)
+    k = _bf16(rng.standard_normal((B, T, Hkv, D)))
+    v = _bf16(rng.standard_normal((B, T, Hkv, D)) * vmul)
+    k8, ks = oracle.kv_quant(k)
+    v8, vs = oracle.kv_quant(v)
+    return q, k8, ks, v, v8, vs
+
+
+def test_int8_v_one_token_gives_back_the_row():
+    # T = 1: weight 1, the output is the stored row rotated back, within the
+    # row's quantization error (|e_i| <= s/2 per rotated element, so at most
+    # sqrt(D) s / 2 = 8 s per output element) plus one BF16 rounding
+    rng = np.random.default_rng(110)
+    q, k8, ks, v, v8, vs = _v8_case(rng, 2, 1, 4, 2, vmul=3.0)
+    o, w = oracle.decode_attn_v8(q, k8, ks, v8, vs, 1)
+    assert (w == 1.0).all()
+    got = oracle.bf16_to_f32(o).astype(np.float64)
+    ref = np.repeat(_f(v)[:, 0], 2, axis=1)                   # heads 0,1 -> KV 0; 2,3 -> KV 1
+    bound = 8 * np.repeat(vs[:, :, 0], 2, axis=1)[..., None] + 2 ** -8 * np.abs(ref)
+    assert (np.abs(got - ref) <= bound).all()
+    # and the whole-row error is far below that per-element bound
+    assert np.sqrt(((got - ref) ** 2).sum(-1)).max() <= 8 * vs.max() * 1.01
+
+
+def test_int8_v_matches_the_rotated_back_matrix_formula():
+    # FP64 reference with scipy's Hadamard matrix: o = HM (sum_t w_t s_t v8_t)
+    rng = np.random.default_rng(111)
+    B, T, Hq, Hkv = 2, 45, 6, 3
+    q, k8, ks, v, v8, vs = _v8_case(rng, B, T, Hq, Hkv)
+    o, w = oracle.decode_attn_v8(q, k8, ks, v8, vs, T)
+    _, w_bf16 = oracle.decode_attn(q, k8, ks, np.zeros((B, Hkv, T, D), np.uint16), T)
+    assert np.array_equal(w, w_bf16)                           # the weights do not depend on V
+    deq = v8.astype(np.float64) * vs[..., None].astype(np.float64)        # [B, Hkv, T, D]
+    r = np.einsum("bht,bhtd->bhd", w, np.repeat(deq, Hq // Hkv, axis=1))
+    ref = np.einsum("ed,bhd->bhe", HM, r)
+    got = oracle.bf16_to_f32(o).astype(np.float64)
+    assert np.abs(got - ref).max() <= 2 ** -8 * np.abs(ref).max()
+    # and it stays within the quantization bound of the BF16-V result
+    o16, _ = oracle.decode_attn(q, k8, ks, np.ascontiguousarray(
+        v.permute(0, 2, 1, 3).contiguous().view(torch.int16).numpy().view(np.uint16)), T)
+    g16 = oracle.bf16_to_f32(o16).astype(np.float64)
+    assert np.abs(got - g16).max() <= 8 * vs.max() + 2 ** -7 * np.abs(g16).max()
+
+
+def test_int8_v_constant_rows_ignore_the_weights():
+    # every cached V row equal: any weights summing to 1 give that row back
+    rng = np.random.default_rng(112)
+    B, T, Hq, Hkv = 1, 33, 4, 1
+    q = _bf16(rng.standard_normal((B, Hq, D)) * 4.0)
+    k8, ks = oracle.kv_quant(_bf16(rng.standard_normal((B, T, Hkv, D))))
+    row = rng.standard_normal(D)
+    v8, vs = oracle.kv_quant(_bf16(np.broadcast_to(row, (B, T, Hkv, D))))
+    o, w = oracle.decode_attn_v8(q, k8, ks, v8, vs, T)
+    assert w.std(axis=-1).min() > 0                            # the weights are not uniform
+    got = oracle.bf16_to_f32(o).astype(np.float64)
+    one, _ = oracle.decode_attn_v8(q, k8[:, :, :1], ks[:, :, :1], v8[:, :, :1], vs[:, :, :1], 1)
+    np.testing.assert_allclose(got, oracle.bf16_to_f32(one).astype(np.float64), rtol=2 ** -7, atol=1e-6)

@@ -193,21 +193,32 @@ sage_status sage_attn_fwd_segmented(const sage_shape *shape, const sage_bufs *bu
  *   k_scale  FP32 [B, Hkv, capacity]             amax / 127 of each rotated row
  *   v        BF16 [B, Hkv, capacity / 8, D, 8]   V in blocks of 8 tokens per
  *            channel: token t, channel d of a (batch, KV head) at
- *            ((t / 8) * D + d) * 8 + t % 8                                   */
+ *            ((t / 8) * D + d) * 8 + t % 8
+ * or, for a cache with INT8 V (v NULL; the same page: a rotated INT8 V needs
+ * the transform once more on the output, which the decode applies):
+ *   v8       INT8 [B, Hkv, capacity / 8, D, 8]   rotated V rows, quantized as
+ *            the K rows are, in the same 8-token blocks per channel
+ *   v_scale  FP32 [B, Hkv, capacity]             amax / 127 of each rotated
+ *            V row
+ * Exactly one of v and v8 is set; v_scale goes with v8.                      */
 typedef struct sage_kv_cache {
     int8_t *k8;
     float *k_scale;
     uint16_t *v;
     int32_t B, Hkv, D, capacity;
+    int8_t *v8;
+    float *v_scale;
 } sage_kv_cache;
 
 /* Writes n new tokens at cache positions [t0, t0 + n): per row (b, t, h) of
  * the BF16 views k and v ([B, n, Hkv, D], unit d stride, 16-byte aligned
  * rows), u = H k / 16, k_scale = max(1e-7, max|u|) / 127,
  * k8 = round-half-even-saturate(u * (127 / max(1e-7, max|u|))), v copied
- * into its blocks (the other tokens of a partly written block keep their
+ * into its blocks, or with INT8 V rotated and quantized by the same formulas
+ * into v8 and v_scale (the other tokens of a partly written block keep their
  * values).
- * Refusals: SAGE_E_NULL, SAGE_E_UNSUPPORTED (D != 256), SAGE_E_SHAPE
+ * Refusals: SAGE_E_NULL (also: both or neither of v and v8 set, or v8
+ * without v_scale), SAGE_E_UNSUPPORTED (D != 256), SAGE_E_SHAPE
  * (B, Hkv, capacity not a multiple of 8, n < 1, t0 < 0 or
  * t0 + n > capacity), SAGE_E_STRIDE,
  * SAGE_E_ALIGN, SAGE_E_HIP. */
@@ -221,6 +232,7 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
  * over cache positions [0, T) of KV head h / (Hq / Hkv):
  *   s_t = ((H q / 16) . k8_t) * k_scale_t / 16,  w = softmax(s),
  *   o = bf16(sum_t w_t v_t)
+ * or with INT8 V:  o = bf16((H / 16) sum_t w_t v_scale_t v8_t)
  * o: BF16 [B, Hq, D] contiguous.  The cache is read once: the work-group of
  * one KV head and a chunk of 128 * ns tokens (ns in 1..16, set from the cache
  * size so that the step has about 512 work-groups) serves its Hq / Hkv query

@@ -267,44 +267,60 @@ def v8_logical(shape: Shape, bufs: Buffers) -> torch.Tensor:
 
 @dataclass
 class KvCache:
-    """Device tensors behind sage_kv_cache (D = 256)."""
-    k8: torch.Tensor         # int8  [B, Hkv, capacity, D], rotated K rows
-    k_scale: torch.Tensor    # f32   [B, Hkv, capacity]
-    v: torch.Tensor          # bf16  [B, Hkv, capacity / 8, D, 8], blocks of 8 tokens per channel
+    """Device tensors behind sage_kv_cache (D = 256): V either BF16 (v) or
+    rotated INT8 with one FP32 scale per (head, token) (v8, v_scale)."""
+    k8: torch.Tensor                            # int8  [B, Hkv, capacity, D], rotated K rows
+    k_scale: torch.Tensor                       # f32   [B, Hkv, capacity]
+    v: Optional[torch.Tensor]                   # bf16  [B, Hkv, capacity / 8, D, 8], 8-token blocks per channel
+    v8: Optional[torch.Tensor] = None           # int8  [B, Hkv, capacity / 8, D, 8], rotated V rows
+    v_scale: Optional[torch.Tensor] = None      # f32   [B, Hkv, capacity]
 
     @classmethod
-    def allocate(cls, B: int, Hkv: int, capacity: int, device, D: int = 256) -> "KvCache":
+    def allocate(cls, B: int, Hkv: int, capacity: int, device, D: int = 256, int8_v: bool = False) -> "KvCache":
         """Zeroed cache; capacity must be a multiple of 8."""
         if capacity % 8:
             raise ValueError("capacity must be a multiple of 8")
-        return cls(torch.zeros((B, Hkv, capacity, D), dtype=torch.int8, device=device),
-                   torch.zeros((B, Hkv, capacity), dtype=torch.float32, device=device),
-                   torch.zeros((B, Hkv, capacity // 8, D, 8), dtype=torch.bfloat16, device=device))
+        k8 = torch.zeros((B, Hkv, capacity, D), dtype=torch.int8, device=device)
+        ks = torch.zeros((B, Hkv, capacity), dtype=torch.float32, device=device)
+        if int8_v:
+            return cls(k8, ks, None, torch.zeros((B, Hkv, capacity // 8, D, 8), dtype=torch.int8, device=device),
+                       torch.zeros((B, Hkv, capacity), dtype=torch.float32, device=device))
+        return cls(k8, ks, torch.zeros((B, Hkv, capacity // 8, D, 8), dtype=torch.bfloat16, device=device))
 
     def v_rows(self) -> torch.Tensor:
-        """The cached V as BF16 [B, Hkv, capacity, D] (a copy)."""
-        B, Hkv, nb, D, _ = self.v.shape
-        return self.v.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nb * 8, D)
+        """The cached V (BF16, or INT8 codes of the rotated rows) as
+        [B, Hkv, capacity, D] (a copy)."""
+        blocks = self.v if self.v is not None else self.v8
+        B, Hkv, nb, D, _ = blocks.shape
+        return blocks.permute(0, 1, 2, 4, 3).reshape(B, Hkv, nb * 8, D)
 
     def c(self) -> SageKvCache:
-        """The C view of the cache, after checking that the three tensors agree:
+        """The C view of the cache, after checking that its tensors agree:
         the C ABI takes their pointers and sizes on trust."""
         if self.k8.dim() != 4:
             raise ValueError("k8 must be an int8 [B, Hkv, capacity, D] tensor")
         B, Hkv, cap, D = self.k8.shape
-        want = ((self.k8, (B, Hkv, cap, D), torch.int8), (self.k_scale, (B, Hkv, cap), torch.float32),
-                (self.v, (B, Hkv, cap // 8, D, 8), torch.bfloat16))
+        if (self.v is None) == (self.v8 is None) or (self.v8 is None) != (self.v_scale is None):
+            raise ValueError("a cache holds either v (BF16) or v8 with v_scale (INT8 V)")
+        want = [(self.k8, (B, Hkv, cap, D), torch.int8), (self.k_scale, (B, Hkv, cap), torch.float32)]
+        if self.v is not None:
+            want.append((self.v, (B, Hkv, cap // 8, D, 8), torch.bfloat16))
+        else:
+            want += [(self.v8, (B, Hkv, cap // 8, D, 8), torch.int8), (self.v_scale, (B, Hkv, cap), torch.float32)]
         for t, shp, dt in want:
             if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"cache tensors must be contiguous GPU tensors: k8 int8 [B, Hkv, capacity, D], "
-                                 f"k_scale float32 [B, Hkv, capacity], v bfloat16 [B, Hkv, capacity/8, D, 8]")
-        return SageKvCache(self.k8.data_ptr(), self.k_scale.data_ptr(), self.v.data_ptr(),
-                           B, Hkv, D, cap)
+                                 f"k_scale float32 [B, Hkv, capacity], v bfloat16 [B, Hkv, capacity/8, D, 8] "
+                                 f"or v8 int8 of that shape with v_scale float32 [B, Hkv, capacity]")
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        return SageKvCache(self.k8.data_ptr(), self.k_scale.data_ptr(), ptr(self.v), B, Hkv, D, cap,
+                           ptr(self.v8), ptr(self.v_scale))
 
 
 def kv_append(cache: KvCache, k, v, t0: int, stream=None) -> None:
-    """Rotate, quantize and store K (BF16 [B, n, Hkv, D]) and copy V at
-    positions [t0, t0 + n) (sage_kv_append)."""
+    """Rotate, quantize and store K (BF16 [B, n, Hkv, D]) and copy V (or, in
+    an INT8 V cache, rotate and quantize it like K) at positions [t0, t0 + n)
+    (sage_kv_append)."""
     kv, vv = _view(k, "k"), _view(v, "v")
     B, Hkv, D = cache.k8.shape[0], cache.k8.shape[1], cache.k8.shape[3]
     if k.shape[0] != B or k.shape[2] != Hkv or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):

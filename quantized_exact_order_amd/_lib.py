@@ -49,7 +49,7 @@ class SageSizes(ctypes.Structure):
 
 class SageKvCache(ctypes.Structure):
     _fields_ = [("k8", vp), ("k_scale", vp), ("v", vp), ("B", i32), ("Hkv", i32), ("D", i32),
-                ("capacity", i32)]
+                ("capacity", i32), ("v8", vp), ("v_scale", vp)]
 
 
 P = ctypes.POINTER

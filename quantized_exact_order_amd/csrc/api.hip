@@ -230,12 +230,14 @@ sage_status sage_attn_fwd_segmented(const sage_shape *shape, const sage_bufs *bu
 namespace {
 
 sage_status check_cache(const sage_kv_cache *c) {
-    if (!c || !c->k8 || !c->k_scale || !c->v) return SAGE_E_NULL;
+    if (!c || !c->k8 || !c->k_scale) return SAGE_E_NULL;
+    if ((c->v != nullptr) == (c->v8 != nullptr) || (c->v8 && !c->v_scale)) return SAGE_E_NULL;
     if (c->D != 256) return SAGE_E_UNSUPPORTED;
     if (c->B < 1 || c->B > 65535 || c->Hkv < 1 || c->capacity < 1) return SAGE_E_SHAPE;
     if (c->capacity % sage::kVBlock != 0) return SAGE_E_SHAPE;
     if ((int64_t)c->B * c->Hkv * c->capacity > (int64_t(1) << 34)) return SAGE_E_SHAPE;
-    if (!aligned16(c->k8) || !aligned16(c->k_scale) || !aligned16(c->v)) return SAGE_E_ALIGN;
+    if (!aligned16(c->k8) || !aligned16(c->k_scale)) return SAGE_E_ALIGN;
+    if (c->v ? !aligned16(c->v) : (!aligned16(c->v8) || !aligned16(c->v_scale))) return SAGE_E_ALIGN;
     return SAGE_OK;
 }
 
@@ -257,6 +259,7 @@ sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, 
     p.k = sage::View{static_cast<const uint16_t *>(k->ptr), k->sb, k->sn, k->sh};
     p.v = sage::View{static_cast<const uint16_t *>(v->ptr), v->sb, v->sn, v->sh};
     p.k8 = cache->k8; p.k_scale = cache->k_scale; p.vc = cache->v;
+    if (!cache->v) { p.v8c = cache->v8; p.v_scale = cache->v_scale; }
     return sage_launch_kv_append(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
 }
 
@@ -294,6 +297,7 @@ sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_
     p.nchunk = (int)nchunk;
     p.q = sage::View{static_cast<const uint16_t *>(q->ptr), q->sb, q->sn, q->sh};
     p.k8 = cache->k8; p.k_scale = cache->k_scale; p.vc = cache->v;
+    if (!cache->v) { p.v8c = cache->v8; p.v_scale = cache->v_scale; }
     p.part = static_cast<float *>(workspace);
     p.o = static_cast<uint16_t *>(o);
     return sage_launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;

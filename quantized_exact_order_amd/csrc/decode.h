@@ -13,13 +13,16 @@ constexpr int kVBlock = 8;
 
 // Appends n rows to the cache at positions [t0, t0 + n): K rotated by the
 // normalized Walsh-Hadamard transform and quantized to INT8 with one FP32
-// scale per (head, token); V copied as BF16 into its 8-token blocks.
+// scale per (head, token); V copied as BF16 into its 8-token blocks, or
+// rotated and quantized as K into INT8 8-token blocks.
 struct KvAppendParams {
     int B, Hkv, D, n, t0, cap, nblk;    // nblk: 8-token blocks touched by [t0, t0 + n)
     View k, v;                          // [B, n, Hkv, D] BF16 views
     int8_t *k8;                         // [B, Hkv, cap, D]
     float *k_scale;                     // [B, Hkv, cap]
-    uint16_t *vc;                       // [B, Hkv, cap / 8, D, 8]
+    uint16_t *vc;                       // [B, Hkv, cap / 8, D, 8], or NULL with INT8 V:
+    int8_t *v8c;                        // [B, Hkv, cap / 8, D, 8] rotated INT8 V
+    float *v_scale;                     // [B, Hkv, cap]
 };
 
 // Single-query attention of each query head over the first T cached tokens.
@@ -29,7 +32,9 @@ struct DecodeParams {
     View q;                             // [B, 1, Hq, D] BF16 view (n = 0)
     const int8_t *k8;
     const float *k_scale;
-    const uint16_t *vc;
+    const uint16_t *vc;                 // BF16 V, or NULL with INT8 V:
+    const int8_t *v8c;                  // rotated INT8 V (the output is rotated back)
+    const float *v_scale;
     float *part;                        // [B, Hq, nchunk, kPartStride]: o partial, max, sum
     uint16_t *o;                        // [B, Hq, D] BF16
 };

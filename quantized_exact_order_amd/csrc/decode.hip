@@ -25,6 +25,11 @@
 //     a lane's B operand.
 // The chunk's softmax partial (max, sum, o) goes to a workspace, and a second
 // kernel combines the chunks in a fixed order.
+// INT8 V (the same page: an INT8 V is rotated like K and needs the transform
+// once more on the output): V rows are rotated and quantized as K rows, into
+// 8-token blocks of bytes; the PV step folds each token's V scale into its
+// weight and widens the bytes to BF16 exactly, and the combine applies the
+// normalized transform (its own inverse) to the output before rounding.
 
 #include "decode.h"
 
@@ -65,22 +70,67 @@ __device__ __forceinline__ void load4(const uint16_t *row, int lane, float x[4])
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Rotates, quantizes and stores K row t (cache position) of head h; one wave.
-__device__ __forceinline__ void append_k_row(const KvAppendParams &p, int b, int h, int t, int lane) {
-    const int64_t c = ((int64_t)b * p.Hkv + h) * p.cap + t;          // cache row
+// Rotates and quantizes one BF16 row of 256 (one wave): returns the INT8
+// values of channels 4 lane .. 4 lane + 3 packed in a word, and the row's
+// amax = max(1e-7, max|u|) (the scale is amax / 127).
+__device__ __forceinline__ uint32_t rot_quant_row(const uint16_t *row, int lane, float &amax) {
     float u[4];
-    load4(p.k.ptr + (int64_t)b * p.k.sb + (int64_t)(t - p.t0) * p.k.sn + (int64_t)h * p.k.sh, lane, u);
+    load4(row, lane, u);
     wht256(u, lane);
     float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
                               __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
     m = wave_max_f(m);
-    const float amax = (m > 1e-7f) ? m : 1e-7f;
+    amax = (m > 1e-7f) ? m : 1e-7f;
     const float mul = 127.0f / amax;
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w |= (uint32_t)(to_i8(u[i] * mul) & 0xff) << (8 * i);
+    return w;
+}
+
+// Row t (cache position) of head h of a new K or V view; one wave.
+__device__ __forceinline__ const uint16_t *new_row(const View &x, int t0, int b, int h, int t) {
+    return x.ptr + (int64_t)b * x.sb + (int64_t)(t - t0) * x.sn + (int64_t)h * x.sh;
+}
+
+// Rotates, quantizes and stores K row t (cache position) of head h; one wave.
+__device__ __forceinline__ void append_k_row(const KvAppendParams &p, int b, int h, int t, int lane) {
+    const int64_t c = ((int64_t)b * p.Hkv + h) * p.cap + t;          // cache row
+    float amax;
+    const uint32_t w = rot_quant_row(new_row(p.k, p.t0, b, h, t), lane, amax);
     reinterpret_cast<uint32_t *>(p.k8 + c * 256)[lane] = w;
     if (lane == 0) p.k_scale[c] = amax / 127.0f;
+}
+
+// INT8 V: the new rows of 8-token block blk, rotated and quantized as K rows,
+// into the block's bytes: lane owns channels 4 lane .. 4 lane + 3, 8 bytes
+// (tokens) each, 32 contiguous bytes.
+__device__ __forceinline__ void append_v8_block(const KvAppendParams &p, int b, int h, int blk, int ta, int te,
+                                                int lane) {
+    const int tb = kVBlock * blk;
+    uint4 *dst = reinterpret_cast<uint4 *>(
+        p.v8c + ((((int64_t)b * p.Hkv + h) * (p.cap / kVBlock) + blk) * 256 + 4 * lane) * kVBlock);
+    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
+    if (te - ta < kVBlock) {
+        w0 = dst[0];
+        w1 = dst[1];
+    }
+    // channel i: tokens 0..3 in wd[i][0], 4..7 in wd[i][1], token e in byte e % 4
+    uint32_t wd[4][2] = {{w0.x, w0.y}, {w0.z, w0.w}, {w1.x, w1.y}, {w1.z, w1.w}};
+    for (int t = ta; t < te; ++t) {
+        float amax;
+        const uint32_t q = rot_quant_row(new_row(p.v, p.t0, b, h, t), lane, amax);
+        const int e = t - tb, sh = 8 * (e & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t byte = ((q >> (8 * i)) & 0xffu) << sh, keep = ~(0xffu << sh);
+            if (e < 4) wd[i][0] = (wd[i][0] & keep) | byte;
+            else wd[i][1] = (wd[i][1] & keep) | byte;
+        }
+        if (lane == 0) p.v_scale[((int64_t)b * p.Hkv + h) * p.cap + t] = amax / 127.0f;
+    }
+    dst[0] = make_uint4(wd[0][0], wd[0][1], wd[1][0], wd[1][1]);
+    dst[1] = make_uint4(wd[2][0], wd[2][1], wd[3][0], wd[3][1]);
 }
 
 // One wave per (b, KV head, 8-token block touched by [t0, t0 + n)): the K rows
@@ -96,6 +146,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) 
     const int tb = kVBlock * blk;
     const int ta = max(tb, p.t0), te = min(tb + kVBlock, p.t0 + p.n);    // new tokens [ta, te)
     for (int t = ta; t < te; ++t) append_k_row(p, b, h, t, lane);
+    if (p.v8c) {
+        append_v8_block(p, b, h, blk, ta, te, lane);
+        return;
+    }
 
     uint4 *dst = reinterpret_cast<uint4 *>(
         p.vc + ((((int64_t)b * p.Hkv + h) * (p.cap / kVBlock) + blk) * 256 + 4 * lane) * kVBlock);
@@ -167,6 +221,32 @@ __device__ __forceinline__ void load_v_step(uint4 vv[16], const uint16_t *vb, in
     }
 }
 
+// INT8 V: the 8 bytes (tokens ts + 8 q4 .. + 7) of channels 16 nb + r16 and
+// the V scales of those tokens; a block past T reads the last valid block
+// (its weights are zero and its scales are not used).
+__device__ __forceinline__ void load_v8_step(uint4 vv[16], float4 &s0, float4 &s1, const int8_t *vb,
+                                             const float *vsb, int ts, int T, int q4, int r16) {
+    const int blk = min(ts / kVBlock + q4, (T - 1) / kVBlock);
+    const int8_t *vr = vb + ((int64_t)blk * 256 + r16) * kVBlock;
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i x = __builtin_nontemporal_load(reinterpret_cast<const v2i *>(vr + nb * 16 * kVBlock));
+        vv[nb] = make_uint4(x[0], x[1], 0u, 0u);
+    }
+    const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(vsb + blk * kVBlock));
+    const v4f c = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(vsb + blk * kVBlock + 4));
+    s0 = make_float4(a[0], a[1], a[2], a[3]);
+    s1 = make_float4(c[0], c[1], c[2], c[3]);
+}
+
+// Two INT8 values (bytes 2 j and 2 j + 1 of w) as a BF16 pair, exactly
+// (integers of magnitude <= 128 have at most 8 significant bits).
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int j) {
+    const float a = (float)(int8_t)(w >> (16 * j)), c = (float)(int8_t)(w >> (16 * j + 8));
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(c) & 0xffff0000u);
+}
+
 // Chunk partial of the grp (<= 16) query heads of one KV head over tokens
 // [128 ns chunk, 128 ns (chunk + 1)).  Grid (nchunk * Hkv, B), 256 threads;
 // step st of wave w covers tokens 128 ns chunk + 128 st + 32 w + [0, 32), so
@@ -179,6 +259,7 @@ __device__ __forceinline__ void load_v_step(uint4 vv[16], const uint16_t *vb, in
 // nontemporal.  The K loads are not: each reads 64 bytes of each of 16 rows
 // (half a cache line per row), and with that shape a nontemporal hint made
 // the step slower (87 against 80 us on the decode workload).
+template <bool kInt8V>
 __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams p) {
     __shared__ __attribute__((aligned(16))) int8_t qp[3][kDecodeMaxGroup][kQRow];   // query parts
     __shared__ float qsc[3][kDecodeMaxGroup];                                        // their scales
@@ -197,6 +278,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     const int8_t *kb = p.k8 + bh * p.cap * 256;
     const float *ksb = p.k_scale + bh * p.cap;
     const uint16_t *vb = p.vc + bh * p.cap * 256;
+    const int8_t *vb8 = p.v8c + bh * p.cap * 256;
+    const float *vsb = p.v_scale + bh * p.cap;
     // the query rows of this wave's heads g = wave + 4 i are loaded first, so
     // that waiting for them does not wait for the step loads issued after
     // (unconditionally: heads g >= grp read head grp - 1, are expanded like
@@ -212,7 +295,9 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     // clamped, valid rows and does not use them)
     KStep k;
     uint4 vv[16];
-    load_v_step(vv, vb, tw, T, q4, r16);
+    float4 vs0, vs1;                        // INT8 V: scales of the lane's 8 tokens
+    if constexpr (kInt8V) load_v8_step(vv, vs0, vs1, vb8, vsb, tw, T, q4, r16);
+    else load_v_step(vv, vb, tw, T, q4, r16);
     load_k_step(k, kb, ksb, tw, T, q4, r16);
     __builtin_amdgcn_sched_barrier(0);      // every load above is issued before the expansion
 
@@ -261,7 +346,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     for (int st = 0; st < nst; ++st) {
         const int ts = tw + 128 * st;
         if (st > 0) {
-            load_v_step(vv, vb, ts, T, q4, r16);
+            if constexpr (kInt8V) load_v8_step(vv, vs0, vs1, vb8, vsb, ts, T, q4, r16);
+            else load_v_step(vv, vb, ts, T, q4, r16);
             load_k_step(k, kb, ksb, ts, T, q4, r16);
         }
 
@@ -327,6 +413,13 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
         uint32_t mk[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) mk[c] = nv >= 2 * c + 2 ? 0xffffffffu : (nv == 2 * c + 1 ? 0x0000ffffu : 0u);
+        if constexpr (kInt8V) {
+            // INT8 V: each token's V scale goes into its weight (tokens past
+            // T get weight 0 whatever their scale slot holds)
+            const float vsc[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = e < nv ? sc[e] * vsc[e] : 0.0f;
+        }
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -338,7 +431,12 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb) {
             uint4 v = vv[nb];
-            v.x &= mk[0]; v.y &= mk[1]; v.z &= mk[2]; v.w &= mk[3];
+            if constexpr (kInt8V) {
+                v = make_uint4(i8x2_to_bf16x2(v.x, 0), i8x2_to_bf16x2(v.x, 1), i8x2_to_bf16x2(v.y, 0),
+                               i8x2_to_bf16x2(v.y, 1));
+            } else {
+                v.x &= mk[0]; v.y &= mk[1]; v.z &= mk[2]; v.w &= mk[3];
+            }
             const v8bf bv = __builtin_bit_cast(v8bf, v);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, bv, o[nb], 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl8, bv, o[nb], 0, 0, 0);
@@ -468,10 +566,25 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
     __syncthreads();
     if (cg == 0) {
         const float t = (((og[0][d] + og[1][d]) + og[2][d]) + og[3][d]) * (1.0f / wmax[0]);
-        const float u = __shfl_xor(t, 1, 64);               // pairs of channels -> one BF16x2 store
-        if ((d & 1) == 0) {
-            uint32_t *dst = reinterpret_cast<uint32_t *>(p.o + ((int64_t)b * p.Hq + h) * 256 + d);
-            *dst = pack_bf16x2(t, u);
+        if (p.v8c) {
+            fw[d] = t;                                      // rotated back below
+        } else {
+            const float u = __shfl_xor(t, 1, 64);           // pairs of channels -> one BF16x2 store
+            if ((d & 1) == 0) {
+                uint32_t *dst = reinterpret_cast<uint32_t *>(p.o + ((int64_t)b * p.Hq + h) * 256 + d);
+                *dst = pack_bf16x2(t, u);
+            }
+        }
+    }
+    if (p.v8c) {
+        // INT8 V holds rotated rows: the normalized transform (its own
+        // inverse) of the combined output gives the output, one wave
+        __syncthreads();
+        if (wave == 0) {
+            float u[4] = {fw[4 * lane], fw[4 * lane + 1], fw[4 * lane + 2], fw[4 * lane + 3]};
+            wht256(u, lane);
+            *reinterpret_cast<uint2 *>(p.o + ((int64_t)b * p.Hq + h) * 256 + 4 * lane) =
+                make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
         }
     }
 }
@@ -487,7 +600,9 @@ hipError_t sage_launch_kv_append(const sage::KvAppendParams &p, hipStream_t s) {
 
 hipError_t sage_launch_decode(const sage::DecodeParams &p, hipStream_t s) {
     if (p.grp < 1 || p.grp > sage::kDecodeMaxGroup) return hipErrorInvalidValue;
-    sage::decode_chunk_kernel<<<dim3((unsigned)(p.nchunk * p.Hkv), p.B), 256, 0, s>>>(p);
+    const dim3 grid((unsigned)(p.nchunk * p.Hkv), p.B);
+    if (p.v8c) sage::decode_chunk_kernel<true><<<grid, 256, 0, s>>>(p);
+    else sage::decode_chunk_kernel<false><<<grid, 256, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     sage::decode_combine_kernel<<<dim3(p.Hq, p.B), sage::kCombineThreads, 0, s>>>(p);

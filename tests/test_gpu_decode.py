@@ -77,22 +77,31 @@ def test_append_in_pieces_equals_one_append():
     assert torch.equal(a.v.view(torch.int16), b.v.view(torch.int16))
 
 
-def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label="", poison=False):
+def _check_decode(B, Hq, Hkv, T, cap, seed, q_scale=1.0, label="", poison=False, int8_v=False):
     import quantized_exact_order_amd as sage
     rng = np.random.default_rng(seed)
+    label = label + (" int8 V" if int8_v else "")
     banner(f"decode {label} B={B} Hq={Hq} Hkv={Hkv} T={T} cap={cap}")
     _, k, v = _kv(rng, B, T, Hkv)
     q = torch.from_numpy((rng.standard_normal((B, Hq, D)) * q_scale).astype(np.float32)).to(torch.bfloat16)
-    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
-    if poison:          # NaN in every V slot, K scale and K byte pattern that the append does not write
-        cache.v.view(torch.int16).fill_(0x7fc0)
+    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda", int8_v=int8_v)
+    if poison:          # NaN in every V slot, K and V scale and K byte pattern that the append does not write
+        if int8_v:
+            cache.v8.fill_(-128)
+            cache.v_scale.view(torch.int32).fill_(0x7fc00000)
+        else:
+            cache.v.view(torch.int16).fill_(0x7fc0)
         cache.k_scale.view(torch.int32).fill_(0x7fc00000)
         cache.k8.fill_(-128)
     sage.kv_append(cache, k.cuda(), v.cuda(), 0)
     o = sage.decode_attn(cache, q.cuda(), T)
     torch.cuda.synchronize()
     k8, ks = oracle.kv_quant(k)
-    o_ref, _ = oracle.decode_attn(q, k8, ks, _v_bits(v.permute(0, 2, 1, 3)), T)
+    if int8_v:
+        v8, vs = oracle.kv_quant(v)
+        o_ref, _ = oracle.decode_attn_v8(q, k8, ks, v8, vs, T)
+    else:
+        o_ref, _ = oracle.decode_attn(q, k8, ks, _v_bits(v.permute(0, 2, 1, 3)), T)
     g = o.cpu().float().numpy().astype(np.float64)
     r = oracle.bf16_to_f32(o_ref).astype(np.float64)
     err = np.abs(g - r)
@@ -245,3 +254,38 @@ def test_decode_step_hip_graph_replays_match_eager():
         assert torch.equal(o.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert torch.equal(cache.k8, k8_eager) and torch.equal(cache.v.view(torch.int16), v_eager.view(torch.int16))
         assert torch.equal(cache.k_scale.view(torch.int32), ks_eager.view(torch.int32)), f"replay {rep}"
+
+
+def test_int8_v_append_matches_oracle_byte_for_byte():
+    # V rows rotated and quantized exactly as K rows, stored in 8-token blocks;
+    # appended in pieces that start and end inside blocks, the other tokens of
+    # a block keep their bytes
+    import quantized_exact_order_amd as sage
+    rng = np.random.default_rng(120)
+    B, n, Hkv, t0, cap = 2, 300, 3, 17, 400
+    banner(f"kv_append int8 V B={B} n={n} Hkv={Hkv} t0={t0}")
+    _, k, v = _kv(rng, B, n, Hkv, scale=3.0)
+    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda", int8_v=True)
+    cache.v8.fill_(0x55)
+    cache.v_scale.fill_(2.0)
+    for s, e in ((0, 1), (1, 70), (70, 131), (131, n)):
+        sage.kv_append(cache, k[:, s:e].cuda(), v[:, s:e].cuda(), t0 + s)
+    torch.cuda.synchronize()
+    k8, ks = oracle.kv_quant(k)
+    v8, vs = oracle.kv_quant(v)
+    assert np.array_equal(cache.k8[:, :, t0:t0 + n].cpu().numpy(), k8)
+    assert np.array_equal(cache.k_scale[:, :, t0:t0 + n].cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    vr = cache.v_rows().cpu().numpy()
+    assert np.array_equal(vr[:, :, t0:t0 + n], v8)
+    assert np.array_equal(cache.v_scale[:, :, t0:t0 + n].cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    assert (vr[:, :, :t0] == 0x55).all() and (vr[:, :, t0 + n:] == 0x55).all()
+    assert (cache.v_scale[:, :, :t0] == 2.0).all() and (cache.v_scale[:, :, t0 + n:] == 2.0).all()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,cap,poison", [
+    (2, 2, 2, 300, 320, False), (2, 16, 2, 300, 320, False), (2, 26, 2, 300, 320, False),
+    (1, 8, 2, 1, 8, True), (1, 8, 2, 9, 16, True), (1, 8, 2, 63, 64, False), (1, 8, 2, 257, 1024, True),
+    (1, 8, 2, 1000, 1000, False), (4, 8, 4, 8200, 8200, True), (4, 16, 4, 20000, 20000, False),
+    (1, 16, 4, 32768, 32768, False)])
+def test_int8_v_decode(B, Hq, Hkv, T, cap, poison):
+    _check_decode(B, Hq, Hkv, T, cap, seed=130 + T + Hq, q_scale=2.0, label="", poison=poison, int8_v=True)

@@ -296,6 +296,12 @@ def run_decode(args):
     step_bytes = cache_bytes + 2 * B * Hq * D * 2
     append_bytes = B * T * Hkv * D * 2 * 2 + cache_bytes   # read K, V BF16; write the cache
     gbps = step_bytes / (t_decode * 1e-3) / 1e9
+    # the same step over a cache with rotated INT8 V (one scale per head and token)
+    cache8 = sage.KvCache.allocate(B, Hkv, T, dev, int8_v=True)
+    t_append8 = timed(lambda: sage.kv_append(cache8, k, v, 0), max(args.steps, 1))
+    t_decode8 = timed(lambda: sage.decode_attn(cache8, q, T, o, ws), reps)
+    step_bytes8 = B * Hkv * T * (D + 4 + D + 4) + 2 * B * Hq * D * 2
+    del cache8
     result = {
         "metric": "decode attention over the INT8 K cache: HBM GB/s (cache bytes / step time)",
         "value": round(gbps, 1),
@@ -313,6 +319,9 @@ def run_decode(args):
         "decode_steps_per_s": round(1e3 / t_decode, 1),
         "append": {"tokens": B * T, "ms": round(t_append, 4),
                    "GB_per_s": round(append_bytes / (t_append * 1e-3) / 1e9, 1)},
+        "int8_v": {"ms_per_step": round(t_decode8, 5), "bytes_per_step": step_bytes8,
+                   "GB_per_s": round(step_bytes8 / (t_decode8 * 1e-3) / 1e9, 1),
+                   "decode_steps_per_s": round(1e3 / t_decode8, 1), "append_ms": round(t_append8, 4)},
     }
     print(json.dumps(result), flush=True)
 

@@ -172,7 +172,18 @@ def test_decode_cache_refusals_happen_before_launch(sage):
     assert append(cache(v=A + 4), 0, 1) == "SAGE_E_ALIGN"
     assert append(cache(capacity=60), 0, 1) == "SAGE_E_SHAPE"   # capacity not a multiple of 8
     assert append(cache(), 0, 1, SageView(A, 0, 512, 256, 2)) == "SAGE_E_STRIDE"
+    # a cache holds BF16 V or INT8 V (v8 with its scales), never both or neither
+    assert append(cache(v=0), 0, 1) == "SAGE_E_NULL"
+    assert append(cache(v8=A), 0, 1) == "SAGE_E_NULL"
+    assert append(cache(v8=A, v_scale=A), 0, 1) == "SAGE_E_NULL"
+    assert append(cache(v=0, v8=A), 0, 1) == "SAGE_E_NULL"
+    assert append(cache(v=0, v8=A + 4, v_scale=A), 0, 1) == "SAGE_E_ALIGN"
+    assert append(cache(v=0, v8=A, v_scale=A + 4), 0, 1) == "SAGE_E_ALIGN"
     n = ctypes.c_size_t()
+    assert name(lib.sage_decode_workspace(ctypes.byref(cache(v=0, v8=A, v_scale=A)), 8, 64, ctypes.byref(n))) \
+        == "SAGE_OK"
+    assert name(lib.sage_decode_workspace(ctypes.byref(cache(v8=A, v_scale=A)), 8, 64, ctypes.byref(n))) \
+        == "SAGE_E_NULL"
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 64, ctypes.byref(n))) == "SAGE_OK"
     assert n.value == 1 * 8 * 1 * 260 * 4 + (-(1 * 8 * 260 * 4) % 256)     # one chunk of partials
     assert name(lib.sage_decode_workspace(ctypes.byref(cache()), 8, 65, ctypes.byref(n))) == "SAGE_E_SHAPE"

@@ -203,7 +203,8 @@ def test_kld_gate_on_gpu_cache(mult):
     assert np.mean(klds) <= 1e-3
 
 
-def test_decode_step_hip_graph_replays_match_eager():
+@pytest.mark.parametrize("int8_v", [False, True])
+def test_decode_step_hip_graph_replays_match_eager(int8_v):
     # one serving step (append one token, then decode over the cache) captured
     # in a HIP graph with caller-owned output and workspace, replayed three
     # times with unrelated eager work between replays that overwrites the
@@ -211,14 +212,16 @@ def test_decode_step_hip_graph_replays_match_eager():
     import quantized_exact_order_amd as sage
     rng = np.random.default_rng(95)
     B, Hq, Hkv, T0, cap = 2, 16, 2, 3000, 3072
-    banner(f"decode step in a HIP graph B={B} Hq={Hq} Hkv={Hkv} T0={T0}")
+    banner(f"decode step in a HIP graph B={B} Hq={Hq} Hkv={Hkv} T0={T0} int8_v={int8_v}")
     _, k, v = _kv(rng, B, T0 + 1, Hkv)
     k, v = k.cuda(), v.cuda()
     q = torch.from_numpy((rng.standard_normal((B, Hq, D)) * 2.0).astype(np.float32)).to(torch.bfloat16).cuda()
     q2 = q.flip(1).contiguous()
-    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda")
+    cache = sage.KvCache.allocate(B, Hkv, cap, "cuda", int8_v=int8_v)
     sage.kv_append(cache, k[:, :T0], v[:, :T0], 0)
     k1, v1 = k[:, T0:], v[:, T0:]
+    vt = (lambda: cache.v.view(torch.int16)) if not int8_v else (lambda: torch.cat(
+        [cache.v8.flatten(), cache.v_scale.view(torch.int8).flatten()]))
     need = max(sage.decode_workspace(cache, Hq, T0 + 1), sage.decode_workspace(cache, Hq, T0))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
@@ -230,7 +233,7 @@ def test_decode_step_hip_graph_replays_match_eager():
     step()
     torch.cuda.synchronize()
     eager = o.clone()
-    k8_eager, ks_eager, v_eager = cache.k8.clone(), cache.k_scale.clone(), cache.v.clone()
+    k8_eager, ks_eager, v_eager = cache.k8.clone(), cache.k_scale.clone(), vt().clone()
     o_full = sage.decode_attn(cache, q, T0 + 1)            # library-allocated buffers: same bytes
     torch.cuda.synchronize()
     assert torch.equal(o_full.view(torch.int16), eager.view(torch.int16))
@@ -246,13 +249,15 @@ def test_decode_step_hip_graph_replays_match_eager():
     for rep in range(3):
         cache.k8[:, :, T0].fill_(7)
         cache.k_scale[:, :, T0].fill_(3.0)
+        if int8_v:
+            cache.v_scale[:, :, T0].fill_(5.0)
         o.zero_()
         sage.decode_attn(cache, q2, T0, o=torch.empty_like(o), workspace=ws)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
-        assert torch.equal(cache.k8, k8_eager) and torch.equal(cache.v.view(torch.int16), v_eager.view(torch.int16))
+        assert torch.equal(cache.k8, k8_eager) and torch.equal(vt(), v_eager)
         assert torch.equal(cache.k_scale.view(torch.int32), ks_eager.view(torch.int32)), f"replay {rep}"
 
 

@@ -138,37 +138,47 @@ def test_decode_multi_step_chunks(B, Hq, Hkv, T, poison):
 
 
 @pytest.mark.timeout(600)
-def test_decode_cache_past_2_31_elements():
+@pytest.mark.parametrize("int8_v", [False, True])
+def test_decode_cache_past_2_31_elements(int8_v):
     # B = 16 sequences x 8 KV heads x 67,000 tokens x 256: the K cache holds
-    # 2.2e9 bytes and V 2.2e9 BF16 values, past 2^31.  The GPU appends and
-    # decodes everything; the oracle quantizes and attends single (b, KV head)
-    # slices, among them the last one at the far end of the cache
+    # 2.2e9 bytes and V 2.2e9 values (BF16 or INT8), past 2^31.  The GPU
+    # appends and decodes everything; the oracle quantizes and attends single
+    # (b, KV head) slices, among them the last one at the far end of the cache
     import quantized_exact_order_amd as sage
     B, Hkv, grp, T = 16, 8, 4, 67000
     Hq = Hkv * grp
-    banner(f"decode cache past 2^31 elements: B={B} Hkv={Hkv} T={T}")
+    banner(f"decode cache past 2^31 elements: B={B} Hkv={Hkv} T={T} int8_v={int8_v}")
     gen = torch.Generator(device="cuda").manual_seed(91)
     k, v = (torch.randn((B, T, Hkv, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(2))
     q = (2.0 * torch.randn((B, Hq, D), generator=gen, device="cuda")).to(torch.bfloat16)
-    cache = sage.KvCache.allocate(B, Hkv, T, "cuda")
+    cache = sage.KvCache.allocate(B, Hkv, T, "cuda", int8_v=int8_v)
     sage.kv_append(cache, k, v, 0)
     o = sage.decode_attn(cache, q, T)
     torch.cuda.synchronize()
-    assert cache.k8.numel() > 2 ** 31 and cache.v.numel() > 2 ** 31
+    vblocks = cache.v8 if int8_v else cache.v
+    assert cache.k8.numel() > 2 ** 31 and vblocks.numel() > 2 ** 31
     for b, hk in ((0, 0), (7, 3), (B - 1, Hkv - 1)):
         ks = k[b:b + 1, :, hk:hk + 1].cpu()
         k8, kscale = oracle.kv_quant(ks)
         assert np.array_equal(cache.k8[b, hk].cpu().numpy(), k8[0, 0]), (b, hk)
         assert np.array_equal(cache.k_scale[b, hk].cpu().numpy().view(np.uint32), kscale[0, 0].view(np.uint32))
-        vs = _v_bits(v[b:b + 1, :, hk:hk + 1].permute(0, 2, 1, 3))
-        vblk = cache.v[b:b + 1, hk:hk + 1]                      # [1, 1, T/8, D, 8] -> [1, 1, T, D]
-        assert np.array_equal(_v_bits(vblk.permute(0, 1, 2, 4, 3).reshape(1, 1, T, D)), vs), (b, hk)
+        vblk = vblocks[b:b + 1, hk:hk + 1].permute(0, 1, 2, 4, 3).reshape(1, 1, T, D)   # [1, 1, T/8, D, 8] -> rows
         qs = q[b:b + 1, hk * grp:(hk + 1) * grp].cpu()
-        o_ref, _ = oracle.decode_attn(qs, k8, kscale, vs, T)
+        if int8_v:
+            v8, vscale = oracle.kv_quant(v[b:b + 1, :, hk:hk + 1].cpu())
+            assert np.array_equal(vblk.cpu().numpy(), v8), (b, hk)
+            assert np.array_equal(cache.v_scale[b, hk].cpu().numpy().view(np.uint32), vscale[0, 0].view(np.uint32))
+            o_ref, _ = oracle.decode_attn_v8(qs, k8, kscale, v8, vscale, T)
+        else:
+            vs = _v_bits(v[b:b + 1, :, hk:hk + 1].permute(0, 2, 1, 3))
+            assert np.array_equal(_v_bits(vblk), vs), (b, hk)
+            o_ref, _ = oracle.decode_attn(qs, k8, kscale, vs, T)
         g = o[b:b + 1, hk * grp:(hk + 1) * grp].cpu().float().numpy().astype(np.float64)
         r = oracle.bf16_to_f32(o_ref).astype(np.float64)
         assert np.abs(g - r).max() <= 2 ** -7 * np.abs(r).max(), (b, hk)
         assert oracle.cosine(g, r) >= 0.99999, (b, hk)
+    del cache, k, v
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(300)

@@ -590,6 +590,24 @@ def main():
             "hbm_peak_GB_per_s": 8000.0,
         },
     }
+    # co-bounds of the attention launch, beside the MFMA roofline:
+    #  - one exp2 per score; the issue floor takes v_exp_f32 at the measured 9.0
+    #    SIMD cycles per wave64 instruction on all 1024 SIMDs at 2.4 GHz;
+    #  - every 128-row query tile streams its head's INT8 K and E4M3 V from
+    #    L2/MALL once (padded key rows);
+    #  - HBM: q8, k8, v8 and their scales read once, O written once.
+    exps = B * Hq * N * N
+    exp_floor_ms = exps / (1024 * (64 / 9.0) * 2.4e9) * 1e3
+    restream = 2 * z.k_rows * D * ((N + 127) // 128) * Hq * B
+    hbm = z.q8 + z.k8 + z.v8 + z.q_scale + z.k_scale + z.v_scale + 2 * B * N * Hq * D
+    t = attn_avg_ms * 1e-3
+    result["co_bounds"] = {
+        "exp2": {"count": exps, "per_s": round(exps / t, 1), "issue_floor_ms": round(exp_floor_ms, 3),
+                 "floor_frac_of_launch": round(exp_floor_ms / attn_avg_ms, 4)},
+        "kv_restream_l2": {"bytes": int(restream), "GB_per_s": round(restream / t / 1e9, 1)},
+        "hbm": {"algorithmic_bytes": int(hbm), "GB_per_s": round(hbm / t / 1e9, 1),
+                "frac": round(hbm / t / 1e9 / 8000.0, 4)},
+    }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, cfg)

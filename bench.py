@@ -289,9 +289,22 @@ def run_decode(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    def per_launch(fn, reps):
+        # one event pair per call: median, min and interquartile range in ms
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, c in ev:
+            a.record()
+            fn()
+            c.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(c) for a, c in ev)
+        return {"median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5),
+                "iqr_ms": [round(t[len(t) // 4], 5), round(t[(3 * len(t)) // 4], 5)]}
+
     reps = max(args.steps, 1) * 10
     t_append = timed(lambda: sage.kv_append(cache, k, v, 0), max(args.steps, 1))
     t_decode = timed(lambda: sage.decode_attn(cache, q, T, o, ws), reps)
+    dist = per_launch(lambda: sage.decode_attn(cache, q, T, o, ws), reps)
     cache_bytes = B * Hkv * T * (D + 4 + 2 * D)            # k8 + k_scale + BF16 V, read once
     step_bytes = cache_bytes + 2 * B * Hq * D * 2
     append_bytes = B * T * Hkv * D * 2 * 2 + cache_bytes   # read K, V BF16; write the cache
@@ -300,6 +313,7 @@ def run_decode(args):
     cache8 = sage.KvCache.allocate(B, Hkv, T, dev, int8_v=True)
     t_append8 = timed(lambda: sage.kv_append(cache8, k, v, 0), max(args.steps, 1))
     t_decode8 = timed(lambda: sage.decode_attn(cache8, q, T, o, ws), reps)
+    dist8 = per_launch(lambda: sage.decode_attn(cache8, q, T, o, ws), reps)
     step_bytes8 = B * Hkv * T * (D + 4 + D + 4) + 2 * B * Hq * D * 2
     del cache8
     result = {
@@ -317,11 +331,13 @@ def run_decode(args):
                      "frac": round(gbps / 8000.0, 4), "bytes_per_step": step_bytes,
                      "kernels": "decode_chunk_kernel + decode_combine_kernel"},
         "decode_steps_per_s": round(1e3 / t_decode, 1),
+        "step_ms_per_launch": dist,
         "append": {"tokens": B * T, "ms": round(t_append, 4),
                    "GB_per_s": round(append_bytes / (t_append * 1e-3) / 1e9, 1)},
         "int8_v": {"ms_per_step": round(t_decode8, 5), "bytes_per_step": step_bytes8,
                    "GB_per_s": round(step_bytes8 / (t_decode8 * 1e-3) / 1e9, 1),
-                   "decode_steps_per_s": round(1e3 / t_decode8, 1), "append_ms": round(t_append8, 4)},
+                   "decode_steps_per_s": round(1e3 / t_decode8, 1), "append_ms": round(t_append8, 4),
+                   "step_ms_per_launch": dist8},
     }
     print(json.dumps(result), flush=True)
 

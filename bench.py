@@ -498,7 +498,7 @@ def main():
                     help="attention launch at the canonical N against the largest tail-free N below it")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path "
+        print(f"bench.py: the benchmark runs on one GPU only (got --gpus {args.gpus}); the path "
               "shards by head with no exchange, so one GPU's throughput is the measured figure.",
               file=sys.stderr)
         sys.exit(2)

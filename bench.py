@@ -49,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense INT8 / FP8 MFMA (5.0 POP/s)
+PEAK_CLOCK_GHZ = 2.4           # the shader clock that peak is quoted at
 METRIC = "attention TFLOPS (4·N²·H·D/t) at N=37810,H=56,D=128; % INT8/FP8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_canonical_traffic.json")
 
@@ -71,6 +72,28 @@ def _traffic():
     if rec.get("source_hash") != _attn_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_clock(sage, shape, bufs, o, stream, launches: int = 2):
+    """Shader clock the attention launch runs at: the stamped variant of the
+    same launch (same kernel, same inputs), run right after the timed region;
+    each work-group's first wave gives (shader cycles) / (constant-counter
+    ticks) x the counter's rate over its lifetime.  Median and interquartile
+    range over the work-groups of the last launch."""
+    import torch
+    hz = sage.wall_clock_hz()
+    for _ in range(launches):
+        st = sage.attn_fwd_stamped(shape, bufs, o, stream)
+    torch.cuda.synchronize()
+    s = st.cpu().numpy().astype("int64")
+    dc, dw = s[:, 2] - s[:, 0], s[:, 3] - s[:, 1]
+    ok = dw > 0
+    ghz = sorted((dc[ok] / dw[ok] * hz / 1e9).tolist())
+    n = len(ghz)
+    return {"GHz": round(ghz[n // 2], 4), "iqr": [round(ghz[n // 4], 4), round(ghz[(3 * n) // 4], 4)],
+            "note": (f"median over {n} work-groups of a stamped launch of the same kernel after the timed "
+                     f"region (s_memtime cycles / s_memrealtime ticks x {hz / 1e6:.0f} MHz); the peak "
+                     f"{PEAK_MFMA_TFLOPS:.0f} TFLOP/s assumes {PEAK_CLOCK_GHZ} GHz")}
 
 
 def _cpu_model():
@@ -567,6 +590,7 @@ def main():
 
     ops = cfg.attn_ops
     achieved = ops / (attn_avg_ms * 1e-3) / 1e12
+    clock = measured_clock(sage, shape, bufs, o, stream)
     result = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
@@ -597,6 +621,11 @@ def main():
             "ops_per_launch": ops,
             "iqr_launch_ms": [round(attn_ms[len(attn_ms) // 4], 4), round(attn_ms[(3 * len(attn_ms)) // 4], 4)],
             "min_launch_ms": round(attn_ms[0], 4),
+            "clock_GHz": clock["GHz"],
+            "clock_GHz_iqr": clock["iqr"],
+            "peak_at_measured_clock": round(PEAK_MFMA_TFLOPS * clock["GHz"] / PEAK_CLOCK_GHZ, 1),
+            "frac_at_measured_clock": round(achieved / (PEAK_MFMA_TFLOPS * clock["GHz"] / PEAK_CLOCK_GHZ), 4),
+            "clock_note": clock["note"],
         },
         "prep": {
             "kernels": "sage_prep + sage_quant_qk (6 launches)",

@@ -156,6 +156,26 @@ sage_status sage_quant_qk(const sage_shape *shape, const sage_view_bf16 *q, cons
 sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
                           int64_t osn, int64_t osh, void *stream);
 
+/* Measurement variant of sage_attn_fwd: the same launch and output, and in
+ * addition the first wave of every work-group reads the shader-clock counter
+ * (s_memtime) and the constant-rate counter (s_memrealtime) when it starts
+ * and when it ends, and writes the four values (uint64: clock at start, wall
+ * at start, clock at end, wall at end) to stamps + 4 * (work-group index).
+ * Cycles over wall ticks, times the constant counter's rate
+ * (sage_wall_clock_khz), is the shader clock the launch ran at.
+ *   stamps       device memory, 16-byte aligned, of at least
+ *                sage_attn_stamp_bytes bytes (32 per work-group of
+ *                128 query rows: B * Hq * ceil(N/128) of them)
+ * Refusals: those of sage_attn_fwd, SAGE_E_NULL, SAGE_E_WORKSPACE (stamps
+ * too small), SAGE_E_ALIGN. */
+sage_status sage_attn_stamp_bytes(const sage_shape *shape, size_t *bytes);
+sage_status sage_attn_fwd_stamped(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
+                                  int64_t osn, int64_t osh, uint64_t *stamps, size_t stamp_bytes, void *stream);
+
+/* Rate of the constant-rate counter of the current device, in kHz
+ * (hipDeviceAttributeWallClockRate).  SAGE_E_NULL, SAGE_E_HIP. */
+sage_status sage_wall_clock_khz(int32_t *khz);
+
 /* Segmented (split-KV) attention: an opt-in mode that is NOT the exact order
  * of sage_attn_fwd.  The contract page forbids combining KV partials; this
  * mode combines them, after the FP8-PV page's segmented schedules, to give

@@ -226,16 +226,19 @@ void oracle_rmsnorm_rope(int B, int N, int H, int D, int R, float eps,
  *   mean  out: FP32 [B, H, D]
  *
  * Reading (the production tree is not frozen on the page): S is the balanced
- * pairwise tree, in natural order, over P = max(64, 2^ceil(log2 N)) leaves,
- * leaf n being zk[n] for n < N and +0.0f for n >= N; mean = S / (float)N.
- * (The same tree is a pairwise tree inside every aligned 64-row block followed
- * by a pairwise tree over the blocks, padded to a power of two with +0.0f.)
+ * pairwise tree, in natural order, over P = 2^ceil(log2 N) leaves (P = 1 for
+ * N = 1), leaf n being zk[n] for n < N and +0.0f for n >= N;
+ * mean = S / (float)N.  For N >= 64 the same tree is a pairwise tree inside
+ * every aligned 64-row block followed by a pairwise tree over the blocks,
+ * padded to a power of two with +0.0f.
  * Pinned by: constant column gives the constant exactly; FP64 mean within
- * FP32 rounding; sum of (z - mean) near zero.
+ * FP32 rounding; sum of (z - mean) near zero; a column of negative zeros over
+ * a power-of-two N has no padding leaf and sums to -0.0 (IEEE 754: the sum of
+ * two zeros of one sign keeps that sign), one more row brings in a +0.0f leaf.
  */
 void oracle_k_mean(int B, int H, int N, int D, const uint16_t *zk, float *mean)
 {
-    int64_t P = 64;
+    int64_t P = 1;
     while (P < N) P *= 2;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; b++)

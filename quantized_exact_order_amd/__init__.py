@@ -28,7 +28,8 @@ from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageKvCache, SageShap
                    SageView, check, lib)
 
 __all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
-           "attn_segmented_workspace", "attn_fwd_segmented", "v8_logical", "v8_slot_keys", "KvCache",
+           "attn_segmented_workspace", "attn_fwd_segmented", "attn_fwd_stamped", "wall_clock_hz",
+           "v8_logical", "v8_slot_keys", "KvCache",
            "kv_append", "decode_workspace", "decode_attn", "selftest_primitive", "SageError", "LIB_PATH",
            "EXPORTS"]
 
@@ -183,6 +184,28 @@ def attn_fwd(shape: Shape, bufs: Buffers, o: Optional[torch.Tensor] = None, stre
     check(lib.sage_attn_fwd(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), o.data_ptr(),
                             sb, sn, sh, _stream(stream)), "sage_attn_fwd")
     return o
+
+
+def attn_fwd_stamped(shape: Shape, bufs: Buffers, o: torch.Tensor, stream=None):
+    """sage_attn_fwd_stamped: the attention launch of attn_fwd, writing o, plus
+    per-work-group clock stamps.  Returns a uint64 tensor [work-groups, 4]:
+    shader clock and constant-rate counter at the start and at the end of the
+    work-group's first wave."""
+    bufs.check(shape)
+    n = ctypes.c_size_t()
+    check(lib.sage_attn_stamp_bytes(ctypes.byref(shape.c()), ctypes.byref(n)), "sage_attn_stamp_bytes")
+    stamps = torch.zeros(n.value // 8, dtype=torch.int64, device=o.device)
+    sb, sn, sh, _ = o.stride()
+    check(lib.sage_attn_fwd_stamped(ctypes.byref(shape.c()), ctypes.byref(bufs.c()), o.data_ptr(), sb, sn, sh,
+                                    stamps.data_ptr(), n.value, _stream(stream)), "sage_attn_fwd_stamped")
+    return stamps.view(-1, 4)
+
+
+def wall_clock_hz() -> float:
+    """Rate of the constant-rate counter of the current device (Hz)."""
+    khz = ctypes.c_int32()
+    check(lib.sage_wall_clock_khz(ctypes.byref(khz)), "sage_wall_clock_khz")
+    return khz.value * 1e3
 
 
 def attn_segmented_workspace(shape: Shape, nseg: int) -> int:

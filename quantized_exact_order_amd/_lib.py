@@ -66,6 +66,12 @@ _lib.sage_attn_segmented_workspace.argtypes = [P(SageShape), i32, P(sz)]
 _lib.sage_attn_segmented_workspace.restype = i32
 _lib.sage_attn_fwd_segmented.argtypes = [P(SageShape), P(SageBufs), i32, vp, i64, i64, i64, vp, sz, vp]
 _lib.sage_attn_fwd_segmented.restype = i32
+_lib.sage_attn_stamp_bytes.argtypes = [P(SageShape), P(sz)]
+_lib.sage_attn_stamp_bytes.restype = i32
+_lib.sage_attn_fwd_stamped.argtypes = [P(SageShape), P(SageBufs), vp, i64, i64, i64, vp, sz, vp]
+_lib.sage_attn_fwd_stamped.restype = i32
+_lib.sage_wall_clock_khz.argtypes = [P(i32)]
+_lib.sage_wall_clock_khz.restype = i32
 _lib.sage_kv_append.argtypes = [P(SageKvCache), P(SageView), P(SageView), i32, i32, vp]
 _lib.sage_kv_append.restype = i32
 _lib.sage_decode_workspace.argtypes = [P(SageKvCache), i32, i32, P(sz)]
@@ -82,6 +88,7 @@ _lib.sage_version.restype = i32
 
 EXPORTS = ("sage_buffer_sizes", "sage_prep", "sage_quant_qk", "sage_attn_fwd",
            "sage_attn_segmented_workspace", "sage_attn_fwd_segmented",
+           "sage_attn_stamp_bytes", "sage_attn_fwd_stamped", "sage_wall_clock_khz",
            "sage_kv_append", "sage_decode_workspace", "sage_decode_attn",
            "sage_selftest_primitive", "sage_v8_key_of_slot", "sage_status_str", "sage_version")
 

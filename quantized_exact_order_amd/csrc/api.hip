@@ -201,6 +201,37 @@ sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *
     return sage_launch_attn(p, shape->D, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
 }
 
+sage_status sage_attn_stamp_bytes(const sage_shape *shape, size_t *bytes) {
+    sage_status st = check_shape(shape);
+    if (st != SAGE_OK) return st;
+    if (!bytes) return SAGE_E_NULL;
+    *bytes = (size_t)shape->B * shape->Hq * (size_t)((shape->N + 127) / 128) * 4 * sizeof(uint64_t);
+    return SAGE_OK;
+}
+
+sage_status sage_attn_fwd_stamped(const sage_shape *shape, const sage_bufs *bufs, void *o, int64_t osb,
+                                  int64_t osn, int64_t osh, uint64_t *stamps, size_t stamp_bytes, void *stream) {
+    sage::AttnParams p;
+    sage_status st = build_attn(shape, bufs, o, osb, osn, osh, &p);
+    if (st != SAGE_OK) return st;
+    size_t need = 0;
+    if ((st = sage_attn_stamp_bytes(shape, &need)) != SAGE_OK) return st;
+    if (!stamps) return SAGE_E_NULL;
+    if (stamp_bytes < need) return SAGE_E_WORKSPACE;
+    if (!aligned16(stamps)) return SAGE_E_ALIGN;
+    p.stamps = stamps;
+    return sage_launch_attn(p, shape->D, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+sage_status sage_wall_clock_khz(int32_t *khz) {
+    if (!khz) return SAGE_E_NULL;
+    int dev = 0, rate = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SAGE_E_HIP;
+    if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return SAGE_E_HIP;
+    *khz = rate;
+    return SAGE_OK;
+}
+
 sage_status sage_attn_segmented_workspace(const sage_shape *shape, int32_t nseg, size_t *bytes) {
     sage_status st = check_shape(shape);
     if (st != SAGE_OK) return st;

@@ -221,6 +221,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
     __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KT];
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][KT];
 
+    const Stamp st0 = stamp_now(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hi = lane >> 5, col = lane & 31;
 
@@ -321,6 +322,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
             }
         }
     }
+    stamp_store(p.stamps, st0);
 }
 
 
@@ -339,11 +341,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnPara
 // inline assembly so that the compiler does not treat it as a store to every
 // LDS buffer (it would then wait for the copy before the next LDS read of any
 // buffer); the copy has no register results, and the kernel waits for it
-// (vmcnt) before a barrier that precedes any read of its destination.  M0 is
-// set here for every copy.
+// (vmcnt) before a barrier that precedes any read of its destination.  The
+// LDS address goes in through an M0 operand constraint, so the compiler
+// itself sets M0 for every copy and knows what it holds.
 __device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
-                 : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -526,6 +528,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][KT];
     __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][KT];
 
+    const Stamp st0 = stamp_now(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, col = lane & 31;
 
@@ -700,6 +703,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
             }
         }
     }
+    stamp_store(p.stamps, st0);
 }
 
 // Combines the segment partials of one output row (segmented schedule):

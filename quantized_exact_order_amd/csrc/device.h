@@ -124,7 +124,27 @@ struct AttnParams {
     int nseg;
     float *seg_ro;
     float *seg_md;
+    // measurement only (NULL otherwise): per work-group, the shader-clock
+    // counter and the constant-rate counter at the start and at the end of
+    // its first wave, 4 x uint64 at stamps + 4 * (hardware block index)
+    uint64_t *stamps;
 };
+
+// Clock stamps of one work-group (see AttnParams::stamps).
+struct Stamp {
+    uint64_t clk, wall;
+};
+__device__ __forceinline__ Stamp stamp_now(const uint64_t *stamps) {
+    if (!stamps) return Stamp{0, 0};
+    return Stamp{(uint64_t)clock64(), (uint64_t)wall_clock64()};
+}
+__device__ __forceinline__ void stamp_store(uint64_t *stamps, const Stamp &s0) {
+    if (stamps && threadIdx.x == 0) {
+        const Stamp s1{(uint64_t)clock64(), (uint64_t)wall_clock64()};
+        uint64_t *dst = stamps + 4 * (int64_t)blockIdx.x;
+        dst[0] = s0.clk; dst[1] = s0.wall; dst[2] = s1.clk; dst[3] = s1.wall;
+    }
+}
 
 }  // namespace sage
 

@@ -264,14 +264,22 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
     __syncthreads();
 
     const int64_t wsoff = (((int64_t)b * p.Hkv + h) * p.nk + t) * D;
+    // The tree has 2^ceil(log2 N) leaves: a sequence of one tile stops after
+    // log2 of that many levels (the value then at v[0] is the whole sum, the
+    // rest of the 64-leaf tree would only add +0 leaves to it).
+    int stop = 1;
+    if (p.nk == 1)
+        while (64 / stop > 1 && 64 / stop >= 2 * p.N) stop *= 2;
     for (int d = tid; d < D; d += kThreads) {
         float v[64];
 #pragma unroll
         for (int r = 0; r < 64; ++r) v[r] = __uint_as_float((uint32_t)zbuf[r * D + d] << 16);
 #pragma unroll
         for (int w = 64; w > 1; w >>= 1) {
+            if (w > stop) {
 #pragma unroll
-            for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+                for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+            }
         }
         p.ws_ksum[wsoff + d] = v[0];
         float m = 0.0f;

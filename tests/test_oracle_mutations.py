@@ -52,6 +52,7 @@ MUTANTS = [
     ("rope_interleaved_pairs", "prep", "float a = y[i], bb = y[i + half];",
      "float a = y[2 * i], bb = y[2 * i + 1];"),
     ("k_mean_over_padded_count", "prep", "* D + d] = S / (float)N;", "* D + d] = S / (float)P;"),
+    ("k_mean_64_leaf_floor", "prep", "int64_t P = 1;\n    while (P < N)", "int64_t P = 64;\n    while (P < N)"),
     ("wht_difference_sign", "prep", "u[j + span] = a - b;", "u[j + span] = b - a;"),
     ("wht_scale_1_over_d", "prep", "float s = (float)(1.0 / sqrt((double)D));",
      "float s = (float)(1.0 / (double)D);"),

@@ -128,6 +128,22 @@ def test_k_mean_constant_column_exact(oracle_lib):
         assert np.all(mean[..., 4:] == 0.0)
 
 
+def test_k_mean_tree_has_no_padding_leaf_at_powers_of_two(oracle_lib):
+    # IEEE 754: the sum of two zeros of the same sign is that zero, and
+    # -0 + +0 = +0 under round-to-nearest.  A column of -0.0 over N = 2^k rows
+    # fills the 2^ceil(log2 N) leaves of the tree exactly, so its sum and mean
+    # are -0.0; one row more brings in a +0.0 padding leaf and gives +0.0.
+    neg0 = np.uint16(0x8000)
+    for N in (1, 2, 16, 32, 64, 128):
+        zk = np.full((1, 1, N, 128), neg0, np.uint16)
+        mean = oracle_lib.k_mean(zk)
+        assert np.all(mean.view(np.uint32) == 0x80000000), N
+    for N in (3, 17, 33, 65):
+        zk = np.full((1, 1, N, 128), neg0, np.uint16)
+        mean = oracle_lib.k_mean(zk)
+        assert np.all(mean.view(np.uint32) == 0), N
+
+
 @pytest.mark.parametrize("N", [1, 50, 64, 1000, 4097])
 def test_k_mean_matches_fp64(oracle_lib, N):
     rng = np.random.default_rng(14)

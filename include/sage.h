@@ -266,6 +266,24 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
 sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
                              void *o, void *workspace, size_t ws_bytes, void *stream);
 
+/* Allocation-free variant of sage_decode_attn, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and output, with the
+ * chunk partials kept in a fixed array that the library holds on each GPU it
+ * runs on (sage_decode_noalloc_max_bytes() bytes, 16 MiB, kept until the
+ * process ends) instead of a caller workspace.  The call itself allocates
+ * nothing.  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (different streams, no ordering between them) race and may
+ * return wrong outputs; calls ordered on one stream are safe, since each call
+ * writes every partial it reads.
+ * Refusals: those of sage_decode_attn, and SAGE_E_WORKSPACE when the call's
+ * partials (sage_decode_workspace bytes) exceed the array. */
+sage_status sage_decode_attn_noalloc(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
+                                     void *o, void *stream);
+
+/* Size in bytes of the fixed per-GPU array of sage_decode_attn_noalloc. */
+size_t sage_decode_noalloc_max_bytes(void);
+
 /* Test hook: applies one device number-format primitive of the preparation
  * kernels, in the exact form they use, to the FP32 values whose bit patterns
  * are first, first + 1, ..., first + count - 1, and writes the results to out

@@ -30,7 +30,8 @@ from ._lib import (EXPORTS, LIB_PATH, SageBufs, SageError, SageKvCache, SageShap
 __all__ = ["Shape", "Buffers", "buffer_sizes", "prep", "quant_qk", "attn_fwd", "forward",
            "attn_segmented_workspace", "attn_fwd_segmented", "attn_fwd_stamped", "wall_clock_hz",
            "v8_logical", "v8_slot_keys", "KvCache",
-           "kv_append", "decode_workspace", "decode_attn", "selftest_primitive", "SageError", "LIB_PATH",
+           "kv_append", "decode_workspace", "decode_attn", "decode_attn_noalloc", "decode_noalloc_max_bytes",
+           "selftest_primitive", "SageError", "LIB_PATH",
            "EXPORTS"]
 
 
@@ -382,3 +383,24 @@ def decode_attn(cache: KvCache, q, T: int, o: Optional[torch.Tensor] = None,
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "sage_decode_attn")
     return o
+
+
+def decode_attn_noalloc(cache: KvCache, q, T: int, o: torch.Tensor, stream=None) -> torch.Tensor:
+    """sage_decode_attn_noalloc: decode_attn with the chunk partials in the
+    library's fixed per-GPU array; the caller passes the output, nothing is
+    allocated.  Calls that overlap on one GPU race on that array."""
+    B, Hq, D = q.shape
+    if B != cache.k8.shape[0] or D != cache.k8.shape[3]:
+        raise ValueError(f"q must have shape [{cache.k8.shape[0]}, Hq, {cache.k8.shape[3]}]")
+    if (o.dtype != torch.bfloat16 or tuple(o.shape) != (B, Hq, D) or not o.is_contiguous()
+            or o.device.type != "cuda"):
+        raise ValueError("o must be a contiguous BF16 [B, Hq, D] GPU tensor")
+    qv = _view(q.unsqueeze(1), "q")
+    check(lib.sage_decode_attn_noalloc(ctypes.byref(cache.c()), Hq, ctypes.byref(qv), T, o.data_ptr(),
+                                       _stream(stream)), "sage_decode_attn_noalloc")
+    return o
+
+
+def decode_noalloc_max_bytes() -> int:
+    """Size of the fixed per-GPU array of decode_attn_noalloc."""
+    return int(lib.sage_decode_noalloc_max_bytes())

@@ -78,6 +78,10 @@ _lib.sage_decode_workspace.argtypes = [P(SageKvCache), i32, i32, P(sz)]
 _lib.sage_decode_workspace.restype = i32
 _lib.sage_decode_attn.argtypes = [P(SageKvCache), i32, P(SageView), i32, vp, vp, sz, vp]
 _lib.sage_decode_attn.restype = i32
+_lib.sage_decode_attn_noalloc.argtypes = [P(SageKvCache), i32, P(SageView), i32, vp, vp]
+_lib.sage_decode_attn_noalloc.restype = i32
+_lib.sage_decode_noalloc_max_bytes.argtypes = []
+_lib.sage_decode_noalloc_max_bytes.restype = sz
 _lib.sage_selftest_primitive.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
 _lib.sage_selftest_primitive.restype = i32
 _lib.sage_v8_key_of_slot.argtypes = [i32]
@@ -90,6 +94,7 @@ EXPORTS = ("sage_buffer_sizes", "sage_prep", "sage_quant_qk", "sage_attn_fwd",
            "sage_attn_segmented_workspace", "sage_attn_fwd_segmented",
            "sage_attn_stamp_bytes", "sage_attn_fwd_stamped", "sage_wall_clock_khz",
            "sage_kv_append", "sage_decode_workspace", "sage_decode_attn",
+           "sage_decode_attn_noalloc", "sage_decode_noalloc_max_bytes",
            "sage_selftest_primitive", "sage_v8_key_of_slot", "sage_status_str", "sage_version")
 
 

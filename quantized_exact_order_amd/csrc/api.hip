@@ -303,8 +303,13 @@ sage_status sage_decode_workspace(const sage_kv_cache *cache, int32_t Hq, int32_
     return SAGE_OK;
 }
 
-sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
-                             void *o, void *workspace, size_t ws_bytes, void *stream) {
+namespace {
+
+// Validates the arguments shared by the decode entry points and fills the
+// kernel parameters (all but the partials buffer); *need gets the bytes of
+// chunk partials the call writes.
+sage_status build_decode(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T, void *o,
+                         sage::DecodeParams *p, size_t *need) {
     sage_status st = check_cache(cache);
     if (st != SAGE_OK) return st;
     if ((st = check_view(q)) != SAGE_OK) return st;
@@ -314,25 +319,49 @@ sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_
     if (Hq % cache->Hkv != 0) return SAGE_E_GQA;
     const int grp = Hq / cache->Hkv;
     if (grp > sage::kDecodeMaxGroup) return SAGE_E_UNSUPPORTED;
-    size_t need = 0;
-    if ((st = sage_decode_workspace(cache, Hq, T, &need)) != SAGE_OK) return st;
-    if (!workspace || ws_bytes < need) return SAGE_E_WORKSPACE;
-    if (!aligned16(workspace)) return SAGE_E_ALIGN;
+    if ((st = sage_decode_workspace(cache, Hq, T, need)) != SAGE_OK) return st;
     const int64_t nchunk = sage::decode_nchunk(cache->B, cache->Hkv, T);
     if (nchunk * cache->Hkv > 2147483647LL) return SAGE_E_SHAPE;
+    std::memset(p, 0, sizeof(*p));
+    p->B = cache->B; p->Hq = Hq; p->Hkv = cache->Hkv; p->grp = grp; p->D = cache->D; p->T = T;
+    p->cap = cache->capacity;
+    p->ns = sage::decode_steps(cache->B, cache->Hkv, T);
+    p->nchunk = (int)nchunk;
+    p->q = sage::View{static_cast<const uint16_t *>(q->ptr), q->sb, q->sn, q->sh};
+    p->k8 = cache->k8; p->k_scale = cache->k_scale; p->vc = cache->v;
+    if (!cache->v) { p->v8c = cache->v8; p->v_scale = cache->v_scale; }
+    p->o = static_cast<uint16_t *>(o);
+    return SAGE_OK;
+}
+
+}  // namespace
+
+sage_status sage_decode_attn(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
+                             void *o, void *workspace, size_t ws_bytes, void *stream) {
     sage::DecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.B = cache->B; p.Hq = Hq; p.Hkv = cache->Hkv; p.grp = grp; p.D = cache->D; p.T = T;
-    p.cap = cache->capacity;
-    p.ns = sage::decode_steps(cache->B, cache->Hkv, T);
-    p.nchunk = (int)nchunk;
-    p.q = sage::View{static_cast<const uint16_t *>(q->ptr), q->sb, q->sn, q->sh};
-    p.k8 = cache->k8; p.k_scale = cache->k_scale; p.vc = cache->v;
-    if (!cache->v) { p.v8c = cache->v8; p.v_scale = cache->v_scale; }
+    size_t need = 0;
+    sage_status st = build_decode(cache, Hq, q, T, o, &p, &need);
+    if (st != SAGE_OK) return st;
+    if (!workspace || ws_bytes < need) return SAGE_E_WORKSPACE;
+    if (!aligned16(workspace)) return SAGE_E_ALIGN;
     p.part = static_cast<float *>(workspace);
-    p.o = static_cast<uint16_t *>(o);
     return sage_launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
 }
+
+sage_status sage_decode_attn_noalloc(const sage_kv_cache *cache, int32_t Hq, const sage_view_bf16 *q, int32_t T,
+                                     void *o, void *stream) {
+    sage::DecodeParams p;
+    size_t need = 0;
+    sage_status st = build_decode(cache, Hq, q, T, o, &p, &need);
+    if (st != SAGE_OK) return st;
+    if (need > sage::kDecodeScratchBytes) return SAGE_E_WORKSPACE;
+    void *scratch_ptr = nullptr;
+    if (sage_decode_scratch(&scratch_ptr) != hipSuccess) return SAGE_E_HIP;
+    p.part = static_cast<float *>(scratch_ptr);
+    return sage_launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK : SAGE_E_HIP;
+}
+
+size_t sage_decode_noalloc_max_bytes(void) { return sage::kDecodeScratchBytes; }
 
 sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream) {
     if (!out) return SAGE_E_NULL;

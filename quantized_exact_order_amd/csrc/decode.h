@@ -60,7 +60,15 @@ inline int64_t decode_ws_bytes(int B, int Hq, int Hkv, int T) {
     return (int64_t)B * Hq * decode_nchunk(B, Hkv, T) * kPartStride * 4;
 }
 
+// Size of the fixed per-GPU array that the allocation-free decode uses in
+// place of the workspace: 16 MiB, 16,131 chunk records, e.g. the partials of
+// B = 4 sequences of 32 query heads over 131,072 cached tokens (8.5 MB).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+
 }  // namespace sage
 
 hipError_t sage_launch_kv_append(const sage::KvAppendParams &p, hipStream_t s);
 hipError_t sage_launch_decode(const sage::DecodeParams &p, hipStream_t s);
+// Device address of the current GPU's fixed decode scratch array, looked up
+// once per device (hipGetSymbolAddress) and kept.
+hipError_t sage_decode_scratch(void **ptr);

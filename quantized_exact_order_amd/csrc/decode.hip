@@ -33,6 +33,8 @@
 
 #include "decode.h"
 
+#include <mutex>
+
 namespace sage {
 namespace {
 
@@ -596,6 +598,40 @@ hipError_t sage_launch_kv_append(const sage::KvAppendParams &p, hipStream_t s) {
     const unsigned items = (unsigned)p.nblk * (unsigned)p.Hkv;
     sage::kv_append_kernel<<<dim3((items + 3) / 4, p.B), 256, 0, s>>>(p);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the chunk partials of one step live in a fixed
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy (kDecodeScratchBytes) until the process ends; every call
+// on that GPU overwrites the partials it reads, so nothing needs clearing, and
+// calls that overlap on one GPU race on the array.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[sage::kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t sage_decode_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // the device address of this GPU's copy; the array's name on the host
+        // is only a stand-in and is never passed to a kernel
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = a;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t sage_launch_decode(const sage::DecodeParams &p, hipStream_t s) {

@@ -30,6 +30,10 @@ both medians and the median of the paired ratios B/A.
 on the same views cut to N = 37,760 (295 x 128 rows: no partial query or key
 tile), the tail-free launch; the difference is what the tails cost.
 
+--workload gqa times the same step on the wide-head grouped-query workload
+(B=1, N=8,192, 16 query heads over 4 KV heads, D=256, normalized
+Walsh-Hadamard rotation of Q and K, RoPE on dims 0-191).
+
 --workload decode times the decode-time INT8 K cache (per-head Hadamard
 rotation, one FP32 scale per (head, token), BF16 V): single-query attention
 of B=4 sequences x 32 query heads over 4 KV heads of D=256 and 32,768 cached
@@ -513,7 +517,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("canonical", "encoder", "decode"), default="canonical")
+    ap.add_argument("--workload", choices=("canonical", "gqa", "encoder", "decode"), default="canonical")
     ap.add_argument("--ab", metavar="OTHER_LIB", default=None,
                     help="paired interleaved A/B of sage_attn_fwd against another build of the library")
     ap.add_argument("--pairs", type=int, default=10, help="A/B pairs (with --ab)")
@@ -533,20 +537,32 @@ def main():
         return run_encoder(args)
     if args.workload == "decode":
         return run_decode(args)
+    if args.workload == "gqa":
+        return run_prefill(args, "gqa")
 
+    return run_prefill(args, "canonical")
+
+
+def run_prefill(args, name):
+    """One step = sage_prep + sage_quant_qk + sage_attn_fwd on the named
+    workload; one JSON line with the attention roofline and the CPU oracle."""
     import torch
     import workloads
     import quantized_exact_order_amd as sage
 
-    cfg = workloads.CONFIGS["canonical"]
-    print(f"[bench] generating canonical inputs N={cfg.N} H={cfg.Hq} D={cfg.D}", file=sys.stderr, flush=True)
+    cfg = workloads.CONFIGS[name]
+    print(f"[bench] generating {name} inputs N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D}", file=sys.stderr,
+          flush=True)
     inp = workloads.make_inputs(cfg)
     dev = torch.device("cuda:0")
-    buf = inp.qkv.to(dev)
     Hq, Hkv, D, B, N = cfg.Hq, cfg.Hkv, cfg.D, cfg.B, cfg.N
-    q = buf[:, :, 0:Hq * D].view(B, N, Hq, D)
-    k = buf[:, :, Hq * D:(Hq + Hkv) * D].view(B, N, Hkv, D)
-    v = buf[:, :, (Hq + Hkv) * D:].view(B, N, Hkv, D)
+    if inp.qkv is not None:
+        buf = inp.qkv.to(dev)
+        q = buf[:, :, 0:Hq * D].view(B, N, Hq, D)
+        k = buf[:, :, Hq * D:(Hq + Hkv) * D].view(B, N, Hkv, D)
+        v = buf[:, :, (Hq + Hkv) * D:].view(B, N, Hkv, D)
+    else:
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     w_q, w_k = inp.w_q.to(dev), inp.w_k.to(dev)
     cos, sin = inp.cos.to(dev).contiguous(), inp.sin.to(dev).contiguous()
     shape = sage.Shape(B, N, Hq, Hkv, D, cfg.rope_dim, cfg.hadamard, cfg.eps)
@@ -591,8 +607,18 @@ def main():
     ops = cfg.attn_ops
     achieved = ops / (attn_avg_ms * 1e-3) / 1e12
     clock = measured_clock(sage, shape, bufs, o, stream)
+    kernel = "attn_ilv_kernel<128, false>" if D == 128 else "attn_ilv256_kernel<false>"
+    if name == "canonical":
+        metric = METRIC
+        workload = ("canonical: B=1 N=37810 H=56 D=128, Q/K/V strided views of one BF16 [N,21504] QKV buffer, "
+                    "RMSNorm+RoPE(0-95), K smoothing, INT8 QK, E4M3 PV, non-causal")
+    else:
+        metric = f"attention TFLOPS (4·N²·Hq·D/t) at N={N},Hq={Hq},Hkv={Hkv},D={D}; % INT8/FP8 MFMA peak"
+        workload = (f"{name}: B={B} N={N} Hq={Hq} Hkv={Hkv} D={D}, RMSNorm+RoPE(0-{cfg.rope_dim - 1})"
+                    + (", normalized Walsh-Hadamard rotation of Q and K" if cfg.hadamard else "")
+                    + ", K smoothing, INT8 QK, E4M3 PV, non-causal")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -604,18 +630,16 @@ def main():
         "vs_baseline": None,
         "dtype": "int8+e4m3",
         "data": "synthetic",
-        "config": {"workload": "canonical: B=1 N=37810 H=56 D=128, Q/K/V strided views of one "
-                               "BF16 [N,21504] QKV buffer, RMSNorm+RoPE(0-95), K smoothing, "
-                               "INT8 QK, E4M3 PV, non-causal",
-                   "B": B, "N": N, "H": Hq, "D": D, "step": "sage_prep+sage_quant_qk+sage_attn_fwd"},
+        "config": {"workload": workload, "B": B, "N": N, "H": Hq, "Hkv": Hkv, "D": D,
+                   "step": "sage_prep+sage_quant_qk+sage_attn_fwd"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_ilv_kernel<128, false>",
+            "kernel": kernel,
             "achieved": round(achieved, 3),
             "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-            "traffic": _traffic(),
+            "traffic": _traffic() if name == "canonical" else None,
             "avg_launch_ms": round(attn_avg_ms, 4),
             "median_launch_ms": round(attn_ms[len(attn_ms) // 2], 4),
             "ops_per_launch": ops,
@@ -638,7 +662,7 @@ def main():
     # co-bounds of the attention launch, beside the MFMA roofline:
     #  - one exp2 per score; the issue floor takes v_exp_f32 at the measured 9.0
     #    SIMD cycles per wave64 instruction on all 1024 SIMDs at 2.4 GHz;
-    #  - every 128-row query tile streams its head's INT8 K and E4M3 V from
+    #  - every 128-row query tile streams its KV head's INT8 K and E4M3 V from
     #    L2/MALL once (padded key rows);
     #  - HBM: q8, k8, v8 and their scales read once, O written once.
     exps = B * Hq * N * N
@@ -655,7 +679,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, cfg)
+        heads = (0, 27, 55) if name == "canonical" else (0, Hq // 2 - 1, Hq - 1)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, heads=heads)
     print(json.dumps(result), flush=True)
 
 

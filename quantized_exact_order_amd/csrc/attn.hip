@@ -41,8 +41,8 @@
 // the PV MFMAs of tile t-1 with the softmax of tile t in fenced slots.  K and
 // V tiles are copied from global memory straight into the swizzled LDS
 // layout (global_load_lds), a full iteration ahead.  Wide heads (D = 256)
-// run attn_wide_kernel, which keeps one tile of scores live to stay within
-// the register file and stages tiles through registers.
+// run attn_ilv256_kernel, the same pipeline with 16 KiB tiles and one wave
+// per SIMD (RO alone is 128 registers per lane).
 // Work-groups are renumbered so that consecutive query tiles of a head run on
 // the same XCD and share its L2.
 
@@ -154,30 +154,6 @@ __device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const
     }
 }
 
-// Register staging of one K or V tile: thread tid moves 16-byte chunks
-// tid, tid + THREADS, ... between global memory and the swizzled LDS layout.
-template <int CH, int THREADS>
-__device__ __forceinline__ void stage_load(v4i (&dst)[CH], const uint8_t *src, int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) dst[i] = *reinterpret_cast<const v4i *>(src + 16 * (tid + THREADS * i));
-}
-template <int D, int CH, int THREADS>
-__device__ __forceinline__ void stage_store_k(const v4i (&src)[CH], uint8_t *kb, int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = tid + THREADS * i;
-        *reinterpret_cast<v4i *>(kb + k_lds<D>(c / (D / 16), c % (D / 16))) = src[i];
-    }
-}
-template <int CH, int THREADS>
-__device__ __forceinline__ void stage_store_v(const v4i (&src)[CH], uint8_t *vb, int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = tid + THREADS * i;
-        *reinterpret_cast<v4i *>(vb + v_lds(c >> 2, c & 3)) = src[i];
-    }
-}
-
 // Segmented (split-KV) schedule, an opt-in mode outside the contract's
 // exact order: the work-group of segment seg runs only the key tiles
 // [seg nk / nseg, (seg + 1) nk / nseg), from the initial state, and keeps its
@@ -209,122 +185,6 @@ __device__ __forceinline__ void store_seg_partial(const AttnParams &p, int b, in
                 make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
     if (hi == 0) *reinterpret_cast<float2 *>(p.seg_md + 2 * row) = make_float2(m, d);
 }
-
-template <int D, int WAVES, bool SEG>
-__global__ __launch_bounds__(64 * WAVES, 1) void attn_wide_kernel(const AttnParams p) {
-    constexpr int THREADS = 64 * WAVES;
-    constexpr int QTILE = 32 * WAVES;                // query rows per work-group
-    constexpr int KS = D / 32;                       // QK k-steps == PV output blocks
-    constexpr int KT = 64 * D;                       // bytes of one K (or V) tile
-    constexpr int CH = KT / 16 / THREADS;            // 16-byte chunks per thread per tile
-    static_assert(CH >= 1 && CH * 16 * THREADS == KT, "tile must split evenly");
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KT];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][KT];
-
-    const Stamp st0 = stamp_now(p.stamps);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hi = lane >> 5, col = lane & 31;
-
-    // XCD-aware renumbering: hardware block i runs on XCD i % 8; give each XCD
-    // a contiguous range of (b, h, query tile) so a head's tiles share an L2.
-    const int total = gridDim.x, nxcd = 8;
-    const int xq = total / nxcd, xr = total % nxcd;
-    const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
-    const int lid = x * xq + min(x, xr) + k;
-    const int nqt = (p.N + QTILE - 1) / QTILE;
-    const int nseg = SEG ? p.nseg : 1;
-    const int qt = lid % nqt, seg = (lid / nqt) % nseg;
-    const int h = (lid / (nqt * nseg)) % p.Hq, b = lid / (nqt * nseg * p.Hq);
-    const int hk = h / p.grp;
-    const int q0 = qt * QTILE + 32 * wave;           // first query row of the wave
-    const int g = q0 >> 5;                           // its Q scale group
-
-    // Q fragment (B operand of the QK MFMA): query q0+col, 16 bytes per k-step.
-    const int8_t *qrow = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + q0 + col) * D + 16 * hi;
-    v4i qf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const v4i *>(qrow + 32 * s);
-    const float qs = (g < p.nq) ? p.q_scale[((int64_t)b * p.Hq + h) * p.nq + g] : 1.0f;
-    const float qc = qs * p.c;
-
-    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
-    const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
-    const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
-    int nk = p.nk;
-    int tail_valid = p.N - 64 * (nk - 1);            // valid keys of the last tile (1..64)
-    if constexpr (SEG) seg_tiles(p, seg, nseg, KT, kbase, vbase, ksc, nk, tail_valid);
-
-    v4i stk[CH], stv[CH];
-    auto tile_src = [&](const uint8_t *base, int t) { return base + (int64_t)min(t, nk - 1) * KT; };
-#define SAGE_LOAD(dst, base, T) stage_load<CH, THREADS>(dst, tile_src(base, T), tid)
-#define SAGE_STORE_K(buf) stage_store_k<D, CH, THREADS>(stk, kbuf[buf], tid)
-#define SAGE_STORE_V(buf) stage_store_v<CH, THREADS>(stv, vbuf[buf], tid)
-
-    v16f acc[KS];
-#pragma unroll
-    for (int i = 0; i < KS; ++i) acc[i] = v16f{};
-    float m = -5000000.0f;
-    float dsum = hi ? 0.0f : 1.0f;                   // d0 = 1 once per row
-
-    // one tile of scores live at a time (wide heads): K(t), V(t) share a
-    // buffer index; tile t+1 is staged while tile t is processed
-    SAGE_LOAD(stk, kbase, 0);
-    SAGE_LOAD(stv, vbase, 0);
-    SAGE_STORE_K(0);
-    SAGE_STORE_V(0);
-    SAGE_LOAD(stk, kbase, 1);
-    SAGE_LOAD(stv, vbase, 1);
-    __syncthreads();
-    for (int t = 0; t < nk - 1; ++t) {
-        const int cur = t & 1;
-        v16i sc0, sc1;
-        qk_tile<D>(kbuf[cur], qf, col, hi, sc0, sc1);
-        softmax_pv<D, false>(sc0, sc1, vbuf[cur], qc * ksc[t], col, hi, 64, m, dsum, acc);
-        SAGE_STORE_K(cur ^ 1);                   // K(t+1), V(t+1) over tile t-1
-        SAGE_STORE_V(cur ^ 1);
-        __syncthreads();
-        SAGE_LOAD(stk, kbase, t + 2);
-        SAGE_LOAD(stv, vbase, t + 2);
-    }
-    const int t = nk - 1;
-    v16i sc0, sc1;
-    qk_tile<D>(kbuf[t & 1], qf, col, hi, sc0, sc1);
-    if (tail_valid < 64)
-        softmax_pv<D, true>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, tail_valid, m, dsum, acc);
-    else
-        softmax_pv<D, false>(sc0, sc1, vbuf[t & 1], qc * ksc[t], col, hi, 64, m, dsum, acc);
-#undef SAGE_LOAD
-#undef SAGE_STORE_K
-#undef SAGE_STORE_V
-
-    // ---- finalize: d over both lane halves, O = bf16((RO * (1/d)) * v_scale)
-    const float dt = dsum + shfl_xor_f(dsum, 32);
-    const int n = q0 + col;
-    if constexpr (SEG) {
-        if (n < p.N) store_seg_partial<D>(p, b, h, seg, nseg, n, hi, acc, m, dt);
-        return;
-    }
-    const float rinv = 1.0f / dt;
-    if (n < p.N) {
-        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
-        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
-#pragma unroll
-        for (int blk = 0; blk < KS; ++blk) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * blk + 8 * r4 + 4 * hi;
-                const float4 sc = *reinterpret_cast<const float4 *>(vs + d0);
-                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc.x;
-                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc.y;
-                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc.z;
-                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc.w;
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-            }
-        }
-    }
-    stamp_store(p.stamps, st0);
-}
-
 
 // ---------------------------------------------------------------------------
 // Interleaved schedule: 4 waves (128 query rows) per work-group, two
@@ -567,7 +427,12 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     // k_scale of tiles t and t+1 while iteration t runs; the one of tile t+2
     // is loaded at its start (ahead of the tile copies, so that waiting for
     // it never waits for them) and used an iteration later
-    float ks0 = ksc[0], ks1 = ksc[min(1, nk - 1)], ks2;
+    // the K scales are read through the constant address space: scalar
+    // loads, waited for with lgkmcnt, so that waiting for a scale never waits
+    // for the tile copies in flight (those are vector-memory loads)
+    typedef const float __attribute__((address_space(4))) *kscale_ptr;
+    const kscale_ptr ksc_s = (kscale_ptr)(uintptr_t)ksc;
+    float ks0 = ksc_s[0], ks1 = ksc_s[min(1, nk - 1)], ks2;
 
     const DmaLane dl = dma_lane(wave, lane);
     const uint32_t kl0 = lds_addr(kbuf[0]) + 1024 * wave, kl1 = lds_addr(kbuf[1]) + 1024 * wave;
@@ -598,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     do {                                                                                       \
         __builtin_amdgcn_s_waitcnt(0x0F70);                                                    \
         __syncthreads();                                                                       \
-        ks2 = ksc[min((T) + 2, nk - 1)];                                                       \
+        ks2 = ksc_s[min((T) + 2, nk - 1)];                                                     \
         job.ksrc = kbase + (int64_t)min((T) + 2, nk - 1) * KT;                                 \
         job.vsrc = vbase + (int64_t)(T) * KT;                                                  \
         job.klds = ((T) & 1) ? kl1 : kl0;                                                      \
@@ -706,6 +571,290 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     stamp_store(p.stamps, st0);
 }
 
+// ---------------------------------------------------------------------------
+// Wide heads (D = 256), interleaved schedule.  RO alone is 128 registers per
+// lane, so a work-group of 4 waves (128 query rows) holds a CU by itself:
+// one wave per SIMD, with the register file of the SIMD to itself.  The
+// software pipeline is that of attn_ilv_kernel with 16 KiB K and V tiles:
+// iteration t holds S(t), P(t-1) and the LDS tiles K(t+1), V(t-1), and issues
+// the 16 QK MFMAs of tile t+1 and the 8 PV MFMAs of tile t-1 among the
+// softmax groups of tile t (two QK and one PV MFMA per group slot), with the
+// per-tile order RO = RO alpha(t) + P(t) V(t) of the one-tile path.
+// ---------------------------------------------------------------------------
+
+// Source offsets of the lane's 16-byte chunks of the first 1 KiB block
+// (block `wave`) that a wave copies of every K and every V tile of D = 256,
+// chosen so that the LDS bytes land in the swizzled positions of k_lds<256>
+// and v_lds.  The wave's further blocks (wave + 4 i) are 16 K rows / 64 V^T
+// rows on, where both swizzles repeat: the same offsets from 4096 i bytes on.
+__device__ __forceinline__ DmaLane dma_lane256(int wave, int lane) {
+    const int r = 4 * wave + (lane >> 4), pos = lane & 15;          // K: row r, chunk position pos
+    const int d = 16 * wave + (lane >> 2), vp = lane & 3;            // V^T: row d, chunk position vp
+    const int hv = ((d >> 1) & 1) ^ (((d >> 2) & 1) << 1) ^ ((d >> 3) & 1);
+    return DmaLane{(uint32_t)(r * 256 + 16 * (pos ^ (r & 15))), (uint32_t)(d * 64 + 16 * (vp ^ hv))};
+}
+
+template <bool PREV, bool NEXT>
+__device__ __forceinline__ void ilv256_step(const v16i &sc0, const v16i &sc1, v16i &sn0, v16i &sn1,
+                                            const v8i &pprev, v8i &pcur, const uint8_t *kt,
+                                            const uint8_t *vt, const v4i (&qf)[8], float fc, float fn,
+                                            int col, int hi, float &m, float &alpha,
+                                            bool &moved, float &dsum, v16f (&acc)[8], const DmaJob &job,
+                                            const DmaLane &dl) {
+    constexpr int D = 256;
+#define SAGE_FENCE __builtin_amdgcn_sched_barrier(0)
+    int a[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { a[r] = sc0[r]; a[16 + r] = sc1[r]; }
+    v8i vf[8];
+    v4i kf[16];
+    auto rd_v = [&](int blk) {
+        if constexpr (PREV) {
+            const int d = 32 * blk + col;
+            const v4i x0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+            const v4i x1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+            vf[blk] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+    };
+    auto mf_v = [&](int blk) {
+        if constexpr (PREV)
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[blk], pprev, acc[blk], 0, 0, 0, 0, 0, 0);
+    };
+    // QK MFMA j: k-step j >> 1 of key block j & 1 (the two chains alternate)
+    auto rd_k = [&](int j) {
+        if constexpr (NEXT)
+            kf[j] = *reinterpret_cast<const v4i *>(kt + k_lds<D>(32 * (j & 1) + col, 2 * (j >> 1) + hi));
+    };
+    auto mf_k = [&](int j) {
+        if constexpr (NEXT) {
+            v16i &sn = (j & 1) ? sn1 : sn0;
+            const v16i c = (j < 2) ? v16i{kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                                          kBias, kBias, kBias, kBias, kBias, kBias, kBias}
+                                   : sn;
+            sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[j], qf[j >> 1], c, 0, 0, 0);
+        }
+    };
+    // the wave's copies of the iteration: blocks i of the K tile (i < 4) and
+    // i - 4 of the V tile
+    auto dma = [&](int i) {
+        if (i < 4) lds_dma16(job.ksrc + 4096 * i, dl.k, job.klds + 4096 * i);
+        else lds_dma16(job.vsrc + 4096 * (i - 4), dl.v, job.vlds + 4096 * (i - 4));
+    };
+    const float nm = -m;
+    int pk[8];
+    auto grp = [&](int q) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = 4 * q + i;
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(a[idx]) - kBiasF, fc, nm));
+            pr[i] = e;
+            dsum = dsum + e;
+        }
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __float_as_int(pr[0]), false);
+        pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+        asm volatile("" ::"v"(pk[q]), "v"(dsum));
+    };
+    const float alpha_c = alpha;
+    const bool moved_c = moved;
+    int x0 = 0;
+
+    rd_k(0); rd_k(1); rd_v(0); grp(0); SAGE_FENCE;
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+        mf_k(2 * q - 2); mf_k(2 * q - 1); mf_v(q - 1); dma(q - 1);
+        rd_k(2 * q); rd_k(2 * q + 1); rd_v(q); grp(q);
+        SAGE_FENCE;
+    }
+    mf_k(14); mf_k(15); mf_v(7); dma(7); SAGE_FENCE;
+    if constexpr (NEXT) x0 = block_max(sn0, -2147483647 - 1);
+    SAGE_FENCE;
+    if constexpr (NEXT) {
+        x0 = block_max(sn1, x0);
+        row_stats(x0, fn, m, alpha, moved, dsum);
+        asm volatile("" ::"v"(m), "v"(alpha), "v"(dsum), "s"((int)moved));
+    }
+    SAGE_FENCE;
+#undef SAGE_FENCE
+    pcur = v8i{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+    if (PREV && moved_c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = acc[i] * alpha_c;
+    }
+}
+
+template <bool SEG>
+__global__ __launch_bounds__(256, 1) void attn_ilv256_kernel(const AttnParams p) {
+    constexpr int D = 256;
+    constexpr int QTILE = 128;
+    constexpr int KS = D / 32;
+    constexpr int KT = 64 * D;
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][KT];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][KT];
+
+    const Stamp st0 = stamp_now(p.stamps);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, col = lane & 31;
+
+    const int total = gridDim.x, nxcd = 8;
+    const int xq = total / nxcd, xr = total % nxcd;
+    const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
+    const int lid = x * xq + min(x, xr) + k;
+    const int nqt = (p.N + QTILE - 1) / QTILE;
+    const int nseg = SEG ? p.nseg : 1;
+    const int qt = lid % nqt, seg = (lid / nqt) % nseg;
+    const int h = (lid / (nqt * nseg)) % p.Hq, b = lid / (nqt * nseg * p.Hq);
+    const int hk = h / p.grp;
+    const int q0 = qt * QTILE + 32 * wave;
+    const int g = q0 >> 5;
+
+    const int8_t *qrow = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + q0 + col) * D + 16 * hi;
+    v4i qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const v4i *>(qrow + 32 * s);
+    const float qs = (g < p.nq) ? p.q_scale[((int64_t)b * p.Hq + h) * p.nq + g] : 1.0f;
+    const float qc = qs * p.c;
+
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
+    const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * D * 64;
+    const float *ksc = p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk;
+    int nk = p.nk;
+    int tail_valid = p.N - 64 * (nk - 1);           // valid keys of the last tile (1..64)
+    if constexpr (SEG) seg_tiles(p, seg, nseg, KT, kbase, vbase, ksc, nk, tail_valid);
+
+    v16f acc[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) acc[i] = v16f{};
+    float m = -5000000.0f, alpha = 1.0f;
+    bool moved = false;
+    float dsum = hi ? 0.0f : 1.0f;
+    typedef const float __attribute__((address_space(4))) *kscale_ptr;
+    const kscale_ptr ksc_s = (kscale_ptr)(uintptr_t)ksc;
+    float ks0 = ksc_s[0], ks1 = ksc_s[min(1, nk - 1)], ks2;
+
+    const DmaLane dl = dma_lane256(wave, lane);
+    const uint32_t kl0 = lds_addr(kbuf[0]) + 1024 * wave, kl1 = lds_addr(kbuf[1]) + 1024 * wave;
+    const uint32_t vl0 = lds_addr(vbuf[0]) + 1024 * wave, vl1 = lds_addr(vbuf[1]) + 1024 * wave;
+    auto copy_tile = [&](const uint8_t *src, uint32_t off, uint32_t lds) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(src + 4096 * i, off, lds + 4096 * i);
+    };
+
+    v16i sa0, sa1, sb0, sb1;
+    v8i pa = {}, pb = {};
+    DmaJob job;
+    if (nk > 1) {
+        copy_tile(kbase, dl.k, kl0);
+        copy_tile(kbase + KT, dl.k, kl1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        qk_tile<D>(kbuf[0], qf, col, hi, sa0, sa1);
+        row_stats(block_max(sa1, block_max(sa0, -2147483647 - 1)), qc * ks0, m, alpha, moved, dsum);
+
+#define SAGE_ILV_SYNC(T)                                                                       \
+    do {                                                                                       \
+        __builtin_amdgcn_s_waitcnt(0x0F70);                                                    \
+        __syncthreads();                                                                       \
+        ks2 = ksc_s[min((T) + 2, nk - 1)];                                                     \
+        job.ksrc = kbase + (int64_t)min((T) + 2, nk - 1) * KT;                                 \
+        job.vsrc = vbase + (int64_t)(T) * KT;                                                  \
+        job.klds = ((T) & 1) ? kl1 : kl0;                                                      \
+        job.vlds = ((T) & 1) ? vl1 : vl0;                                                      \
+    } while (0)
+#define SAGE_ILV_ARGS qf, qc * ks0, qc * ks1, col, hi, m, alpha, moved, dsum, acc, job, dl
+#define SAGE_STEP_EVEN(P, N, T)                                                                \
+    ilv256_step<P, N>(sa0, sa1, sb0, sb1, pb, pa, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
+#define SAGE_STEP_ODD(P, N, T)                                                                 \
+    ilv256_step<P, N>(sb0, sb1, sa0, sa1, pa, pb, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
+#define SAGE_NEXT_SCALE do { ks0 = ks1; ks1 = ks2; } while (0)
+        const int tp = nk - 2;
+        SAGE_ILV_SYNC(0);
+        if (tp == 0) SAGE_STEP_EVEN(false, false, 0);
+        else SAGE_STEP_EVEN(false, true, 0);
+        SAGE_NEXT_SCALE;
+        int t = 1;
+        for (; t + 1 < tp; t += 2) {
+            SAGE_ILV_SYNC(t);
+            SAGE_STEP_ODD(true, true, t);
+            SAGE_NEXT_SCALE;
+            SAGE_ILV_SYNC(t + 1);
+            SAGE_STEP_EVEN(true, true, t + 1);
+            SAGE_NEXT_SCALE;
+        }
+        if (t < tp) {
+            SAGE_ILV_SYNC(t);
+            SAGE_STEP_ODD(true, true, t);
+            SAGE_NEXT_SCALE;
+            ++t;
+        }
+        if (tp > 0) {
+            SAGE_ILV_SYNC(tp);
+            if (tp & 1) SAGE_STEP_ODD(true, false, tp);
+            else SAGE_STEP_EVEN(true, false, tp);
+            SAGE_NEXT_SCALE;
+        }
+#undef SAGE_ILV_SYNC
+#undef SAGE_ILV_ARGS
+#undef SAGE_STEP_EVEN
+#undef SAGE_STEP_ODD
+#undef SAGE_NEXT_SCALE
+        // drain: PV of tile tp, and the copy of V(nk-1) into the buffer of V(tp-1)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        copy_tile(vbase + (int64_t)(nk - 1) * KT, dl.v, (nk - 1) & 1 ? vl1 : vl0);
+        {
+            const uint8_t *vt = vbuf[tp & 1];
+            const v8i pl = (tp & 1) ? pb : pa;
+#pragma unroll
+            for (int blk = 0; blk < KS; ++blk) {
+                const int d = 32 * blk + col;
+                const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+                const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+                const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+                acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pl, acc[blk], 0, 0, 0, 0, 0, 0);
+            }
+        }
+    } else {
+        copy_tile(kbase, dl.k, kl0);
+        copy_tile(vbase, dl.v, vl0);
+    }
+    // the last tile (K(nk-1) was copied two iterations ahead, V(nk-1) above)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    {
+        const int tl = nk - 1;
+        v16i s0, s1;
+        qk_tile<D>(kbuf[tl & 1], qf, col, hi, s0, s1);
+        softmax_pv<D, true>(s0, s1, vbuf[tl & 1], qc * ksc[tl], col, hi, tail_valid, m, dsum, acc);
+    }
+
+    const float dt = dsum + shfl_xor_f(dsum, 32);
+    const int n = q0 + col;
+    if constexpr (SEG) {
+        if (n < p.N) store_seg_partial<D>(p, b, h, seg, nseg, n, hi, acc, m, dt);
+        return;
+    }
+    const float rinv = 1.0f / dt;
+    if (n < p.N) {
+        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
+        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * blk + 8 * r4 + 4 * hi;
+                const float4 sc = *reinterpret_cast<const float4 *>(vs + d0);
+                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc.x;
+                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc.y;
+                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc.z;
+                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc.w;
+                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            }
+        }
+    }
+    stamp_store(p.stamps, st0);
+}
+
 // Combines the segment partials of one output row (segmented schedule):
 // M = max_s m_s, a_s = exp2(m_s - M), d = sum_s d_s a_s and RO = sum_s RO_s a_s
 // (from 0, in increasing s), then O = bf16((RO * (1/d)) * v_scale) as in the
@@ -749,9 +898,8 @@ hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s) {
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
         sage::attn_ilv_kernel<128, false><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
-        constexpr int W = 4;
-        const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
-        sage::attn_wide_kernel<256, W, false><<<dim3(nqt * p.Hq * p.B), 64 * W, 0, s>>>(p);
+        const unsigned nqt = (unsigned)((p.N + 127) / 128);
+        sage::attn_ilv256_kernel<false><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
     }
     return hipGetLastError();
 }
@@ -761,9 +909,8 @@ hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStrea
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
         sage::attn_ilv_kernel<128, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
-        constexpr int W = 4;
-        const unsigned nqt = (unsigned)((p.N + 32 * W - 1) / (32 * W));
-        sage::attn_wide_kernel<256, W, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 64 * W, 0, s>>>(p);
+        const unsigned nqt = (unsigned)((p.N + 127) / 128);
+        sage::attn_ilv256_kernel<true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

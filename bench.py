@@ -607,7 +607,7 @@ def run_prefill(args, name):
     ops = cfg.attn_ops
     achieved = ops / (attn_avg_ms * 1e-3) / 1e12
     clock = measured_clock(sage, shape, bufs, o, stream)
-    kernel = "attn_ilv_kernel<128, false>" if D == 128 else "attn_ilv256_kernel<false>"
+    kernel = "attn_ilv_kernel<128, false>" if D == 128 else "attn_pair256_kernel<false>"
     if name == "canonical":
         metric = METRIC
         workload = ("canonical: B=1 N=37810 H=56 D=128, Q/K/V strided views of one BF16 [N,21504] QKV buffer, "

@@ -41,10 +41,13 @@
 // the PV MFMAs of tile t-1 with the softmax of tile t in fenced slots.  K and
 // V tiles are copied from global memory straight into the swizzled LDS
 // layout (global_load_lds), a full iteration ahead.  Wide heads (D = 256)
-// run attn_ilv256_kernel, the same pipeline with 16 KiB tiles and one wave
-// per SIMD (RO alone is 128 registers per lane).
+// run attn_pair256_kernel: each 32-row block is shared by a pair of waves
+// that split every 64-key tile's softmax and the 256 output channels between
+// them, exchanging the half-tile maxima and FP8 probabilities through LDS.
 // Work-groups are renumbered so that consecutive query tiles of a head run on
 // the same XCD and share its L2.
+
+#include <type_traits>
 
 #include "device.h"
 
@@ -571,22 +574,11 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     stamp_store(p.stamps, st0);
 }
 
-// ---------------------------------------------------------------------------
-// Wide heads (D = 256), interleaved schedule.  RO alone is 128 registers per
-// lane, so a work-group of 4 waves (128 query rows) holds a CU by itself:
-// one wave per SIMD, with the register file of the SIMD to itself.  The
-// software pipeline is that of attn_ilv_kernel with 16 KiB K and V tiles:
-// iteration t holds S(t), P(t-1) and the LDS tiles K(t+1), V(t-1), and issues
-// the 16 QK MFMAs of tile t+1 and the 8 PV MFMAs of tile t-1 among the
-// softmax groups of tile t (two QK and one PV MFMA per group slot), with the
-// per-tile order RO = RO alpha(t) + P(t) V(t) of the one-tile path.
-// ---------------------------------------------------------------------------
-
 // Source offsets of the lane's 16-byte chunks of the first 1 KiB block
 // (block `wave`) that a wave copies of every K and every V tile of D = 256,
 // chosen so that the LDS bytes land in the swizzled positions of k_lds<256>
-// and v_lds.  The wave's further blocks (wave + 4 i) are 16 K rows / 64 V^T
-// rows on, where both swizzles repeat: the same offsets from 4096 i bytes on.
+// and v_lds.  A block 4 i further on is 16 i K rows / 64 i V^T rows on, where
+// both swizzles repeat: the same offsets from 4096 i bytes on.
 __device__ __forceinline__ DmaLane dma_lane256(int wave, int lane) {
     const int r = 4 * wave + (lane >> 4), pos = lane & 15;          // K: row r, chunk position pos
     const int d = 16 * wave + (lane >> 2), vp = lane & 3;            // V^T: row d, chunk position vp
@@ -594,107 +586,43 @@ __device__ __forceinline__ DmaLane dma_lane256(int wave, int lane) {
     return DmaLane{(uint32_t)(r * 256 + 16 * (pos ^ (r & 15))), (uint32_t)(d * 64 + 16 * (vp ^ hv))};
 }
 
-template <bool PREV, bool NEXT>
-__device__ __forceinline__ void ilv256_step(const v16i &sc0, const v16i &sc1, v16i &sn0, v16i &sn1,
-                                            const v8i &pprev, v8i &pcur, const uint8_t *kt,
-                                            const uint8_t *vt, const v4i (&qf)[8], float fc, float fn,
-                                            int col, int hi, float &m, float &alpha,
-                                            bool &moved, float &dsum, v16f (&acc)[8], const DmaJob &job,
-                                            const DmaLane &dl) {
-    constexpr int D = 256;
-#define SAGE_FENCE __builtin_amdgcn_sched_barrier(0)
-    int a[32];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { a[r] = sc0[r]; a[16 + r] = sc1[r]; }
-    v8i vf[8];
-    v4i kf[16];
-    auto rd_v = [&](int blk) {
-        if constexpr (PREV) {
-            const int d = 32 * blk + col;
-            const v4i x0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
-            const v4i x1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
-            vf[blk] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        }
-    };
-    auto mf_v = [&](int blk) {
-        if constexpr (PREV)
-            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[blk], pprev, acc[blk], 0, 0, 0, 0, 0, 0);
-    };
-    // QK MFMA j: k-step j >> 1 of key block j & 1 (the two chains alternate)
-    auto rd_k = [&](int j) {
-        if constexpr (NEXT)
-            kf[j] = *reinterpret_cast<const v4i *>(kt + k_lds<D>(32 * (j & 1) + col, 2 * (j >> 1) + hi));
-    };
-    auto mf_k = [&](int j) {
-        if constexpr (NEXT) {
-            v16i &sn = (j & 1) ? sn1 : sn0;
-            const v16i c = (j < 2) ? v16i{kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
-                                          kBias, kBias, kBias, kBias, kBias, kBias, kBias}
-                                   : sn;
-            sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[j], qf[j >> 1], c, 0, 0, 0);
-        }
-    };
-    // the wave's copies of the iteration: blocks i of the K tile (i < 4) and
-    // i - 4 of the V tile
-    auto dma = [&](int i) {
-        if (i < 4) lds_dma16(job.ksrc + 4096 * i, dl.k, job.klds + 4096 * i);
-        else lds_dma16(job.vsrc + 4096 * (i - 4), dl.v, job.vlds + 4096 * (i - 4));
-    };
-    const float nm = -m;
-    int pk[8];
-    auto grp = [&](int q) {
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = 4 * q + i;
-            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(a[idx]) - kBiasF, fc, nm));
-            pr[i] = e;
-            dsum = dsum + e;
-        }
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __float_as_int(pr[0]), false);
-        pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
-        asm volatile("" ::"v"(pk[q]), "v"(dsum));
-    };
-    const float alpha_c = alpha;
-    const bool moved_c = moved;
-    int x0 = 0;
-
-    rd_k(0); rd_k(1); rd_v(0); grp(0); SAGE_FENCE;
-#pragma unroll
-    for (int q = 1; q < 8; ++q) {
-        mf_k(2 * q - 2); mf_k(2 * q - 1); mf_v(q - 1); dma(q - 1);
-        rd_k(2 * q); rd_k(2 * q + 1); rd_v(q); grp(q);
-        SAGE_FENCE;
-    }
-    mf_k(14); mf_k(15); mf_v(7); dma(7); SAGE_FENCE;
-    if constexpr (NEXT) x0 = block_max(sn0, -2147483647 - 1);
-    SAGE_FENCE;
-    if constexpr (NEXT) {
-        x0 = block_max(sn1, x0);
-        row_stats(x0, fn, m, alpha, moved, dsum);
-        asm volatile("" ::"v"(m), "v"(alpha), "v"(dsum), "s"((int)moved));
-    }
-    SAGE_FENCE;
-#undef SAGE_FENCE
-    pcur = v8i{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
-    if (PREV && moved_c) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = acc[i] * alpha_c;
-    }
-}
+// ---------------------------------------------------------------------------
+// Wide heads (D = 256), key-split wave pairs.  A work-group of 8 waves holds
+// 128 query rows; the 32 rows of row block rb belong to the pair of waves rb
+// (half 0) and rb + 4 (half 1), which share a SIMD.  Half hh computes, for its
+// rows, the scores of keys [32 hh, 32 hh + 32) of every 64-key tile, their
+// exponentials, its part of the denominator, and RO for output channels
+// [128 hh, 128 hh + 128).  The pair exchanges through LDS, once per tile and
+// behind the tile's barrier, the two half-tile maxima of each row (the tile
+// maximum is the larger: the same value as over the whole tile) and the
+// packed FP8 probabilities of its keys, so that each wave's PV MFMA sees all
+// 64 keys of the tile.  Per tile and per row the operations are those of the
+// one-wave schedule: the same m, alpha and p, RO of a channel rescaled and
+// accumulated in the same order; the denominator is kept as two partial sums
+// (one per half of the keys, each rescaled by alpha) that are added at the
+// end, as the contract page's own kernel keeps it spread over lanes.  RO is 64
+// registers per lane, so two waves share a SIMD and the rescale is plain VALU.
+// Iteration t: QK of tile t+1 (8 INT8 MFMAs on the wave's key block), the
+// statistics and exponentials of tile t, PV of tile t-1 (4 FP8 MFMAs), the
+// half maximum of tile t+1.
+// ---------------------------------------------------------------------------
 
 template <bool SEG>
-__global__ __launch_bounds__(256, 1) void attn_ilv256_kernel(const AttnParams p) {
+__global__ __launch_bounds__(512, 1) void attn_pair256_kernel(const AttnParams p) {
     constexpr int D = 256;
     constexpr int QTILE = 128;
-    constexpr int KS = D / 32;
-    constexpr int KT = 64 * D;
+    constexpr int KS = D / 32;                       // QK k-steps
+    constexpr int KT = 64 * D;                       // bytes of one K (or V) tile
     __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][KT];
     __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][KT];
+    __shared__ __attribute__((aligned(16))) v4i pbuf[2][8][64];   // packed P of each wave, by tile parity
+    __shared__ int mbuf[2][8][32];                                 // half-tile maxima (biased), by tile parity
+    __shared__ float dbuf[8][32];                                  // final partial denominators
 
     const Stamp st0 = stamp_now(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, col = lane & 31;
+    const int rb = wave & 3, hh = wave >> 2, partner = wave ^ 4;
 
     const int total = gridDim.x, nxcd = 8;
     const int xq = total / nxcd, xr = total % nxcd;
@@ -705,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void attn_ilv256_kernel(const AttnParams p)
     const int qt = lid % nqt, seg = (lid / nqt) % nseg;
     const int h = (lid / (nqt * nseg)) % p.Hq, b = lid / (nqt * nseg * p.Hq);
     const int hk = h / p.grp;
-    const int q0 = qt * QTILE + 32 * wave;
+    const int q0 = qt * QTILE + 32 * rb;
     const int g = q0 >> 5;
 
     const int8_t *qrow = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + q0 + col) * D + 16 * hi;
@@ -721,133 +649,240 @@ __global__ __launch_bounds__(256, 1) void attn_ilv256_kernel(const AttnParams p)
     int nk = p.nk;
     int tail_valid = p.N - 64 * (nk - 1);           // valid keys of the last tile (1..64)
     if constexpr (SEG) seg_tiles(p, seg, nseg, KT, kbase, vbase, ksc, nk, tail_valid);
-
-    v16f acc[KS];
-#pragma unroll
-    for (int i = 0; i < KS; ++i) acc[i] = v16f{};
-    float m = -5000000.0f, alpha = 1.0f;
-    bool moved = false;
-    float dsum = hi ? 0.0f : 1.0f;
     typedef const float __attribute__((address_space(4))) *kscale_ptr;
     const kscale_ptr ksc_s = (kscale_ptr)(uintptr_t)ksc;
-    float ks0 = ksc_s[0], ks1 = ksc_s[min(1, nk - 1)], ks2;
 
+    // copies: the wave's blocks wave and wave + 8 of a 16 KiB tile
     const DmaLane dl = dma_lane256(wave, lane);
-    const uint32_t kl0 = lds_addr(kbuf[0]) + 1024 * wave, kl1 = lds_addr(kbuf[1]) + 1024 * wave;
-    const uint32_t vl0 = lds_addr(vbuf[0]) + 1024 * wave, vl1 = lds_addr(vbuf[1]) + 1024 * wave;
-    auto copy_tile = [&](const uint8_t *src, uint32_t off, uint32_t lds) {
+    const uint32_t kl[2] = {lds_addr(kbuf[0]) + 1024 * wave, lds_addr(kbuf[1]) + 1024 * wave};
+    const uint32_t vl[2] = {lds_addr(vbuf[0]) + 1024 * wave, lds_addr(vbuf[1]) + 1024 * wave};
+    auto copy_k = [&](int t, int buf) {
+        const uint8_t *src = kbase + (int64_t)t * KT;
+        lds_dma16(src, dl.k, kl[buf]);
+        lds_dma16(src + 8192, dl.k, kl[buf] + 8192);
+    };
+    auto copy_v = [&](int t, int buf) {
+        const uint8_t *src = vbase + (int64_t)t * KT;
+        lds_dma16(src, dl.v, vl[buf]);
+        lds_dma16(src + 8192, dl.v, vl[buf] + 8192);
+    };
+    // scores of the wave's key block of tile t (LDS buffer kb), biased: the
+    // first MFMA of the chain reads the bias block, kept in registers
+    const v16i biasv = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                        kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
+    auto qk_half = [&](const uint8_t *kb, v16i &s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(src + 4096 * i, off, lds + 4096 * i);
+        for (int st = 0; st < KS; ++st) {
+            const v4i kf = *reinterpret_cast<const v4i *>(kb + k_lds<D>(32 * hh + col, 2 * st + hi));
+            s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[st], st == 0 ? biasv : s, 0, 0, 0);
+        }
+    };
+    // the key (within the tile) that register r of the wave's block holds
+    auto key_of = [&](int r) { return 32 * hh + 8 * (r >> 2) + 4 * hi + (r & 3); };
+    // row maximum over the wave's 32 keys (both lane halves), keys >= nvalid left out
+    auto half_max = [&](const v16i &s, int nvalid) {
+        int mx;
+        if (nvalid >= 64) {
+            mx = block_max(s, -2147483647 - 1);
+        } else {
+            mx = -2147483647 - 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = (key_of(r) < nvalid) ? max(mx, s[r]) : mx;
+        }
+        return max_xor32(mx);
+    };
+    // the row's denominator: the part of the wave's keys (the page's d0 = 1
+    // counted once, in half 0), and its maximum m
+    float dsum = (hh == 0 && hi == 0) ? 1.0f : 0.0f;
+    float m = -5000000.0f;
+    v16f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = v16f{};
+    // RO += P V for the wave's 128 channels: P of all 64 keys (own 4 registers
+    // and the partner's), V of the tile in LDS buffer vb
+    auto pv = [&](const uint8_t *vb, const v4i &own, const v4i &other) {
+        const v4i lo = hh ? other : own, up = hh ? own : other;
+        const v8i pb = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int d = 128 * hh + 32 * blk + col;
+            const v4i va0 = *reinterpret_cast<const v4i *>(vb + v_lds(d, 2 * hi));
+            const v4i va1 = *reinterpret_cast<const v4i *>(vb + v_lds(d, 2 * hi + 1));
+            const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[blk], 0, 0, 0, 0, 0, 0);
+        }
     };
 
-    v16i sa0, sa1, sb0, sb1;
-    v8i pa = {}, pb = {};
-    DmaJob job;
-    if (nk > 1) {
-        copy_tile(kbase, dl.k, kl0);
-        copy_tile(kbase + KT, dl.k, kl1);
+    // prologue: K(0) (and K(1)) resident, the half maxima of tile 0 exchanged
+    copy_k(0, 0);
+    if (nk > 1) copy_k(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // S(t) and S(t+1) alternate between two register sets (iteration t
+    // reads the set of its parity and writes the other), so nothing is copied
+    v16i sa, sb;
+    qk_half(kbuf[0], sa);
+    int mh = half_max(sa, nk == 1 ? tail_valid : 64);
+    if (hi == 0) mbuf[0][wave][col] = mh;
+    v4i pk_prev = {}, pk_cur;
+    float ks_cur = ksc_s[0];
+    // One iteration in fenced slots: the eight QK MFMAs of tile t+1 one per
+    // slot, each beside a group of VALU work of tile t (statistics, the four
+    // groups of four exponentials) or a PV MFMA of tile t-1; LDS fragment
+    // reads a slot ahead of their MFMA.  Compile-time variants: the parity of
+    // t (which LDS buffers), whether tile t is the last (its keys >= N are
+    // masked), whether tile t+1 exists and whether it is the last.
+    auto iter = [&](int t, const v16i &scur, v16i &snext, auto par_c, auto maskcur_c, auto hasnext_c,
+                    auto masknext_c) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr bool MASKCUR = decltype(maskcur_c)::value, HASNEXT = decltype(hasnext_c)::value;
+        constexpr bool MASKNEXT = decltype(masknext_c)::value;
+#define SAGE_FENCE __builtin_amdgcn_sched_barrier(0)
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        qk_tile<D>(kbuf[0], qf, col, hi, sa0, sa1);
-        row_stats(block_max(sa1, block_max(sa0, -2147483647 - 1)), qc * ks0, m, alpha, moved, dsum);
-
-#define SAGE_ILV_SYNC(T)                                                                       \
-    do {                                                                                       \
-        __builtin_amdgcn_s_waitcnt(0x0F70);                                                    \
-        __syncthreads();                                                                       \
-        ks2 = ksc_s[min((T) + 2, nk - 1)];                                                     \
-        job.ksrc = kbase + (int64_t)min((T) + 2, nk - 1) * KT;                                 \
-        job.vsrc = vbase + (int64_t)(T) * KT;                                                  \
-        job.klds = ((T) & 1) ? kl1 : kl0;                                                      \
-        job.vlds = ((T) & 1) ? vl1 : vl0;                                                      \
-    } while (0)
-#define SAGE_ILV_ARGS qf, qc * ks0, qc * ks1, col, hi, m, alpha, moved, dsum, acc, job, dl
-#define SAGE_STEP_EVEN(P, N, T)                                                                \
-    ilv256_step<P, N>(sa0, sa1, sb0, sb1, pb, pa, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
-#define SAGE_STEP_ODD(P, N, T)                                                                 \
-    ilv256_step<P, N>(sb0, sb1, sa0, sa1, pa, pb, kbuf[((T) + 1) & 1], vbuf[((T) + 1) & 1], SAGE_ILV_ARGS)
-#define SAGE_NEXT_SCALE do { ks0 = ks1; ks1 = ks2; } while (0)
-        const int tp = nk - 2;
-        SAGE_ILV_SYNC(0);
-        if (tp == 0) SAGE_STEP_EVEN(false, false, 0);
-        else SAGE_STEP_EVEN(false, true, 0);
-        SAGE_NEXT_SCALE;
-        int t = 1;
-        for (; t + 1 < tp; t += 2) {
-            SAGE_ILV_SYNC(t);
-            SAGE_STEP_ODD(true, true, t);
-            SAGE_NEXT_SCALE;
-            SAGE_ILV_SYNC(t + 1);
-            SAGE_STEP_EVEN(true, true, t + 1);
-            SAGE_NEXT_SCALE;
-        }
-        if (t < tp) {
-            SAGE_ILV_SYNC(t);
-            SAGE_STEP_ODD(true, true, t);
-            SAGE_NEXT_SCALE;
-            ++t;
-        }
-        if (tp > 0) {
-            SAGE_ILV_SYNC(tp);
-            if (tp & 1) SAGE_STEP_ODD(true, false, tp);
-            else SAGE_STEP_EVEN(true, false, tp);
-            SAGE_NEXT_SCALE;
-        }
-#undef SAGE_ILV_SYNC
-#undef SAGE_ILV_ARGS
-#undef SAGE_STEP_EVEN
-#undef SAGE_STEP_ODD
-#undef SAGE_NEXT_SCALE
-        // drain: PV of tile tp, and the copy of V(nk-1) into the buffer of V(tp-1)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        copy_tile(vbase + (int64_t)(nk - 1) * KT, dl.v, (nk - 1) & 1 ? vl1 : vl0);
-        {
-            const uint8_t *vt = vbuf[tp & 1];
-            const v8i pl = (tp & 1) ? pb : pa;
+        __syncthreads();                                        // K(t+1), V(t-1) resident; exchange written
+        const uint8_t *kb = kbuf[PAR ^ 1], *vb = vbuf[PAR ^ 1];
+        const int mp = mbuf[PAR][partner][col];
+        const v4i pp = pbuf[PAR ^ 1][partner][lane];
+        const float ks_next = ksc_s[min(t + 1, nk - 1)];
+        v4i kf[KS];
+        v8i vf[4];
+        auto rd_k = [&](int st) {
+            if constexpr (HASNEXT)
+                kf[st] = *reinterpret_cast<const v4i *>(kb + k_lds<D>(32 * hh + col, 2 * st + hi));
+        };
+        auto mf_k = [&](int st) {
+            if constexpr (HASNEXT)
+                snext = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[st], qf[st], st == 0 ? biasv : snext, 0, 0, 0);
+        };
+        auto rd_v = [&](int blk) {
+            const int d = 128 * hh + 32 * blk + col;
+            const v4i x0 = *reinterpret_cast<const v4i *>(vb + v_lds(d, 2 * hi));
+            const v4i x1 = *reinterpret_cast<const v4i *>(vb + v_lds(d, 2 * hi + 1));
+            vf[blk] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        };
+        const v4i plo = hh ? pp : pk_prev, pup = hh ? pk_prev : pp;
+        const v8i pfull = {plo[0], plo[1], plo[2], plo[3], pup[0], pup[1], pup[2], pup[3]};
+        const bool first = t == 0;
+        auto mf_v = [&](int blk) {
+            if (!first)
+                acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[blk], pfull, acc[blk], 0, 0, 0, 0,
+                                                                          0, 0);
+        };
+        const float f = qc * ks_cur;
+        float nm = 0.0f, alpha = 1.0f;
+        bool moved = false;
+        auto stats = [&]() {
+            const int mx = max(mh, mp);
+            const float M = (__int_as_float(mx) - kBiasF) * f - 8.807f;
+            const float mnew = __builtin_fmaxf(m, M);
+            alpha = __builtin_amdgcn_exp2f(m - mnew);
+            moved = __any(mnew != m);
+            m = mnew;
+            nm = -mnew;
+            dsum = dsum * alpha;
+        };
+        auto grp = [&](int q) {
+            float pr[4];
 #pragma unroll
-            for (int blk = 0; blk < KS; ++blk) {
-                const int d = 32 * blk + col;
-                const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
-                const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
-                const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
-                acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pl, acc[blk], 0, 0, 0, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q + i;
+                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(scur[r]) - kBiasF, f, nm));
+                if (MASKCUR && key_of(r) >= tail_valid) e = 0.0f;
+                pr[i] = e;
+                dsum = dsum + e;
             }
+            const int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], __float_as_int(pr[0]), false);
+            pk_cur[q] = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+            asm volatile("" ::"v"(pk_cur[q]), "v"(dsum));
+        };
+        rd_k(0); rd_k(1); rd_v(0);
+        if (t + 2 < nk) copy_k(t + 2, PAR);
+        copy_v(t, PAR);
+        SAGE_FENCE;
+        mf_k(0); rd_k(2); stats(); SAGE_FENCE;
+        mf_k(1); rd_k(3); rd_v(1); grp(0); SAGE_FENCE;
+        mf_k(2); rd_k(4); mf_v(0); grp(1); SAGE_FENCE;
+        mf_k(3); rd_k(5); rd_v(2); grp(2); SAGE_FENCE;
+        mf_k(4); rd_k(6); mf_v(1); grp(3); SAGE_FENCE;
+        pbuf[PAR][wave][lane] = pk_cur;
+        mf_k(5); rd_k(7); rd_v(3); SAGE_FENCE;
+        mf_k(6); mf_v(2); SAGE_FENCE;
+        mf_k(7); mf_v(3); SAGE_FENCE;
+        if (moved) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = acc[i] * alpha;
         }
-    } else {
-        copy_tile(kbase, dl.k, kl0);
-        copy_tile(vbase, dl.v, vl0);
+        if constexpr (HASNEXT) {
+            mh = half_max(snext, MASKNEXT ? tail_valid : 64);
+            if (hi == 0) mbuf[PAR ^ 1][wave][col] = mh;
+        }
+        pk_prev = pk_cur;
+        ks_cur = ks_next;
+#undef SAGE_FENCE
+    };
+    using F = std::integral_constant<bool, false>;
+    using T = std::integral_constant<bool, true>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // steady state: neither tile t nor tile t+1 is the last; then the last
+    // one to three iterations (t is even when the loop ends)
+    int t = 0;
+    for (; t + 3 < nk; t += 2) {
+        iter(t, sa, sb, P0(), F(), T(), F());
+        iter(t + 1, sb, sa, P1(), F(), T(), F());
     }
-    // the last tile (K(nk-1) was copied two iterations ahead, V(nk-1) above)
+    if (nk - t == 1) {
+        iter(t, sa, sb, P0(), T(), F(), F());
+    } else if (nk - t == 2) {
+        iter(t, sa, sb, P0(), F(), T(), T());
+        iter(t + 1, sb, sa, P1(), T(), F(), F());
+    } else {
+        iter(t, sa, sb, P0(), F(), T(), F());
+        iter(t + 1, sb, sa, P1(), F(), T(), T());
+        iter(t + 2, sa, sb, P0(), T(), F(), F());
+    }
+    // drain: PV of the last tile (V(nk-1) copied in the last iteration)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     {
-        const int tl = nk - 1;
-        v16i s0, s1;
-        qk_tile<D>(kbuf[tl & 1], qf, col, hi, s0, s1);
-        softmax_pv<D, true>(s0, s1, vbuf[tl & 1], qc * ksc[tl], col, hi, tail_valid, m, dsum, acc);
+        const int pl = (nk - 1) & 1;
+        const v4i pp = pbuf[pl][partner][lane];
+        pv(vbuf[pl], pk_prev, pp);
     }
-
-    const float dt = dsum + shfl_xor_f(dsum, 32);
+    // the row's denominator: both lane halves of both waves of the pair
+    const float dw = dsum + shfl_xor_f(dsum, 32);
+    if (hi == 0) dbuf[wave][col] = dw;
+    __syncthreads();
+    const float dt = (hh == 0) ? dw + dbuf[partner][col] : dbuf[partner][col] + dw;
     const int n = q0 + col;
     if constexpr (SEG) {
-        if (n < p.N) store_seg_partial<D>(p, b, h, seg, nseg, n, hi, acc, m, dt);
+        if (n < p.N) {
+            const int64_t row = (((int64_t)b * p.Hq + h) * nseg + seg) * p.N + n;
+            float *ro = p.seg_ro + row * D + 128 * hh;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<float4 *>(ro + 32 * blk + 8 * r4 + 4 * hi) =
+                        make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
+            if (hi == 0 && hh == 0) *reinterpret_cast<float2 *>(p.seg_md + 2 * row) = make_float2(m, dt);
+        }
         return;
     }
     const float rinv = 1.0f / dt;
     if (n < p.N) {
-        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
-        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
+        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh + 128 * hh;
+        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D + 128 * hh;
 #pragma unroll
-        for (int blk = 0; blk < KS; ++blk) {
+        for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d0 = 32 * blk + 8 * r4 + 4 * hi;
-                const float4 sc = *reinterpret_cast<const float4 *>(vs + d0);
-                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc.x;
-                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc.y;
-                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc.z;
-                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc.w;
+                const float4 sc4 = *reinterpret_cast<const float4 *>(vs + d0);
+                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc4.x;
+                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc4.y;
+                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc4.z;
+                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc4.w;
                 *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
             }
         }
@@ -899,7 +934,7 @@ hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s) {
         sage::attn_ilv_kernel<128, false><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
-        sage::attn_ilv256_kernel<false><<<dim3(nqt * p.Hq * p.B), 256, 0, s>>>(p);
+        sage::attn_pair256_kernel<false><<<dim3(nqt * p.Hq * p.B), 512, 0, s>>>(p);
     }
     return hipGetLastError();
 }
@@ -910,7 +945,7 @@ hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStrea
         sage::attn_ilv_kernel<128, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);
     } else {
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
-        sage::attn_ilv256_kernel<true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);
+        sage::attn_pair256_kernel<true><<<dim3(nqt * p.nseg * p.Hq * p.B), 512, 0, s>>>(p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -300,11 +300,14 @@ size_t sage_decode_noalloc_max_bytes(void);
  *   kind 7  2.25f / x (V multiplier)                    float  [count]
  *   kind 8  2^x as the attention kernel's softmax       float  [count]
  *           computes it (v_exp_f32)
+ *   kind 9  OCP E4M3 as the V cast converts (hardware  uint8  [count]
+ *           conversion; equal to kind 2 for |x| < 448
+ *           and NaN; the V cast's values stay below 2.25)
  * For tests that compare these roundings with an independent implementation
  * over every FP32 pattern (Preparation; Q And K Quantization; V And PV), and
  * that measure the accuracy of the softmax exponential (Online Softmax).
  * Refusals: SAGE_E_NULL, SAGE_E_ALIGN, SAGE_E_UNSUPPORTED (kind outside
- * 0..8), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
+ * 0..9), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
  * SAGE_E_HIP. */
 sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream);
 

@@ -64,6 +64,21 @@ __device__ __forceinline__ uint32_t to_e4m3(float x) {
     return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Four FP32 values -> four OCP E4M3 bytes (value i in byte i), equal to
+// to_e4m3 of each for every value of magnitude below 448 and for NaN, which
+// is all a caller may pass (the scaled V of the preparation is at most 2.25
+// in magnitude).  The hardware conversion (v_cvt_pk_fp8_f32, round to nearest
+// even) gives to_e4m3's byte for every such finite value; for a NaN it writes
+// 0xFF whatever the sign, a byte no finite value below 448 produces, so a word
+// holding one is redone with to_e4m3.
+__device__ __forceinline__ uint32_t pack4_e4m3_bounded(const float (&x)[4]) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+    if ((~r - 0x01010101u) & r & 0x80808080u)              // some byte is 0xFF
+        r = to_e4m3(x[0]) | (to_e4m3(x[1]) << 8) | (to_e4m3(x[2]) << 16) | (to_e4m3(x[3]) << 24);
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // Lane exchanges (wave64).
 // ---------------------------------------------------------------------------

@@ -579,26 +579,30 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
     for (int pass = 0; pass < NPASS; ++pass)
         *reinterpret_cast<uint4 *>(&vbuf[(pass * RPP + rr) * D + 8 * j]) = vraw[pass];
     __syncthreads();
+    // thread: channel pair (2 dp, 2 dp + 1) and a quarter qr of the 64 slots;
+    // for each slot, one 4-byte LDS read gives both channels of its key
     const float *amax = p.ws_vamax + ((int64_t)b * p.Hkv + h) * D;
     uint8_t *dst = p.v8 + (((int64_t)b * p.Hkv + h) * p.nk + t) * (int64_t)D * 64;
     for (int e = tid; e < 2 * D; e += kThreads) {
-        const int d = e >> 1, half = e & 1;
-        const float mul = 2.25f / amax[d];
-        uint32_t w[8];
+        const int dp = e % (D / 2), qr = e / (D / 2);
+        const int d = 2 * dp;
+        const float mul0 = 2.25f / amax[d], mul1 = 2.25f / amax[d + 1];
+        uint32_t w0[4], w1[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint32_t word = 0;
+        for (int k = 0; k < 4; ++k) {
+            float x0[4], x1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = sage_v8_slot_key(32 * half + 4 * k + i);
-                const float x = __uint_as_float((uint32_t)vbuf[key * D + d] << 16);
-                word |= to_e4m3(x * mul) << (8 * i);
+                const int key = sage_v8_slot_key(16 * qr + 4 * k + i);
+                const uint32_t pair = *reinterpret_cast<const uint32_t *>(&vbuf[key * D + d]);
+                x0[i] = bf16_lo(pair) * mul0;
+                x1[i] = bf16_hi(pair) * mul1;
             }
-            w[k] = word;
+            w0[k] = pack4_e4m3_bounded(x0);
+            w1[k] = pack4_e4m3_bounded(x1);
         }
-        uint4 *o = reinterpret_cast<uint4 *>(dst + (int64_t)d * 64 + 32 * half);
-        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        *reinterpret_cast<uint4 *>(dst + (int64_t)d * 64 + 16 * qr) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4 *>(dst + (int64_t)(d + 1) * 64 + 16 * qr) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
     }
 }
 

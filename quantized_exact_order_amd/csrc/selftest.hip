@@ -16,6 +16,8 @@
 //   7  V multiplier  2.25f / x                             -> float
 //   8  softmax exponential, the attention kernel's v_exp_f32 -> float
 //      (not a bit-exact output: its accuracy is measured, not pinned)
+//   9  OCP E4M3 as the V cast converts (pack4_e4m3_bounded) -> uint8
+//      (equal to kind 2 for NaN and below 448 in magnitude)
 
 #include "device.h"
 
@@ -35,6 +37,11 @@ __global__ __launch_bounds__(256) void primitive_kernel(int kind, uint32_t first
     case 5: static_cast<float *>(out)[i] = 127.0f / x; break;
     case 6: static_cast<float *>(out)[i] = x / 2.25f; break;
     case 7: static_cast<float *>(out)[i] = 2.25f / x; break;
+    case 9: {
+        const float v[4] = {x, 0.0f, 0.0f, 0.0f};
+        static_cast<uint8_t *>(out)[i] = (uint8_t)(pack4_e4m3_bounded(v) & 0xffu);
+        break;
+    }
     default: static_cast<float *>(out)[i] = __builtin_amdgcn_exp2f(x); break;
     }
 }

@@ -181,11 +181,14 @@ def run_encoder(args):
             sage.quant_qk(one, bufs1[l], *a)
             sage.attn_fwd(one, bufs1[l], o1[l:l + 1], st)
 
-    # segmented (split-KV, non-exact) schedule for the single-layer calls:
-    # 2, 3 and 6 segments (192 to 576 work-groups instead of 96)
+    # segmented (split-KV, non-exact) schedule: up to 8 segments of a short
+    # sequence run as the waves of one work-group and combine in LDS; 12
+    # takes the two-launch form (partials in HBM, then a combine launch)
     nk = (N + 63) // 64
-    seg_counts = [n for n in (2, 3, 6) if n <= nk]
-    ws_seg = torch.empty(max(sage.attn_segmented_workspace(one, n) for n in seg_counts),
+    seg_counts = [n for n in (2, 3, 4, 6, 8, 12) if n <= nk]
+    stacked_counts = [n for n in (2, 3, 4) if n <= nk]
+    ws_seg = torch.empty(max([sage.attn_segmented_workspace(one, n) for n in seg_counts]
+                             + [sage.attn_segmented_workspace(stacked, n) for n in stacked_counts]),
                          dtype=torch.uint8, device=dev)
     o_seg = torch.empty((L, N, H, D), dtype=torch.bfloat16, device=dev)
 
@@ -196,6 +199,9 @@ def run_encoder(args):
                 sage.attn_fwd_segmented(one, bufs1[l], nseg, o_seg[l:l + 1], ws_seg, st)
             else:
                 sage.attn_fwd(one, bufs1[l], o1[l:l + 1], st)
+
+    def stacked_segmented(nseg):
+        sage.attn_fwd_segmented(stacked, bufsL, nseg, o_seg, ws_seg, torch.cuda.current_stream())
 
     attn_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
@@ -259,6 +265,10 @@ def run_encoder(args):
     for n in seg_counts:
         t_attn[f"nseg={n}"] = timed(lambda: attn_only(n), reps)
         seg_err[f"nseg={n}"] = float((o_seg.float() - ref.float()).abs().max())
+    t_stacked_seg, stacked_seg_err = {}, {}
+    for n in stacked_counts:
+        t_stacked_seg[f"nseg={n}"] = timed(lambda: stacked_segmented(n), reps)
+        stacked_seg_err[f"nseg={n}"] = float((o_seg.float() - ref.float()).abs().max())
     ops = L * 4 * N * N * H * D
     best = min(t_layers, t_graph, t_batched)
     result = {
@@ -281,6 +291,8 @@ def run_encoder(args):
         "segmented_non_exact": {
             "attention_only_ms_per_27_layers": {k: round(t, 4) for k, t in t_attn.items()},
             "max_abs_vs_exact": seg_err,
+            "stacked_27_attention_ms": {k: round(t, 4) for k, t in t_stacked_seg.items()},
+            "stacked_max_abs_vs_exact": stacked_seg_err,
         },
     }
     print(json.dumps(result), flush=True)

@@ -47,6 +47,7 @@
 // Work-groups are renumbered so that consecutive query tiles of a head run on
 // the same XCD and share its L2.
 
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -92,11 +93,24 @@ __device__ __forceinline__ void qk_tile(const uint8_t *kt, const v4i (&qf)[D / 3
     }
 }
 
+// The PV A operand (V^T, channels 32 blk + col, the lane half's 32 keys) of
+// a tile in the swizzled LDS layout.
+struct VfragLds {
+    const uint8_t *vt;
+    int col, hi;
+    __device__ __forceinline__ v8i operator()(int blk) const {
+        const int d = 32 * blk + col;
+        const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
+        const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
+        return v8i{va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
+    }
+};
+
 // Online-softmax update and PV for one tile.  TAIL: keys >= nvalid masked.
-template <int D, bool TAIL>
-__device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const uint8_t *vt, float f,
-                                           int col, int hi, int nvalid, float &m, float &dsum,
-                                           v16f (&acc)[D / 32]) {
+// vfrag(blk) gives the PV A operand of channel block blk.
+template <int D, bool TAIL, typename VFrag>
+__device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const VFrag &vfrag, float f,
+                                           int hi, int nvalid, float &m, float &dsum, v16f (&acc)[D / 32]) {
     int a[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) { a[r] = s0[r]; a[16 + r] = s1[r]; }
@@ -148,12 +162,33 @@ __device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const
         for (int i = 0; i < D / 32; ++i) acc[i] = acc[i] * alpha;
     }
 #pragma unroll
-    for (int blk = 0; blk < D / 32; ++blk) {
-        const int d = 32 * blk + col;
-        const v4i va0 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi));
-        const v4i va1 = *reinterpret_cast<const v4i *>(vt + v_lds(d, 2 * hi + 1));
-        const v8i va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
-        acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[blk], 0, 0, 0, 0, 0, 0);
+    for (int blk = 0; blk < D / 32; ++blk)
+        acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vfrag(blk), pb, acc[blk], 0, 0, 0, 0, 0, 0);
+}
+
+// Final BF16 row of the lane's query: O = (RO / d) x V scale for channels
+// 32 blk + 8 r4 + 4 hi + 0..3.  All the V-scale loads go out before the first
+// store, so the wave waits for them once (a store between two loads would
+// make each load wait for the store ahead of it).
+template <int NB>
+__device__ __forceinline__ void store_o_row(uint16_t *orow, const float *vs, int hi, const v16f (&acc)[NB],
+                                            float rinv) {
+    float4 sc[NB][4];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) sc[blk][r4] = *reinterpret_cast<const float4 *>(vs + 32 * blk + 8 * r4 + 4 * hi);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = 32 * blk + 8 * r4 + 4 * hi;
+            const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc[blk][r4].x;
+            const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc[blk][r4].y;
+            const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc[blk][r4].z;
+            const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc[blk][r4].w;
+            *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        }
     }
 }
 
@@ -544,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
         const int tl = nk - 1;
         v16i s0, s1;
         qk_tile<D>(kbuf[tl & 1], qf, col, hi, s0, s1);
-        softmax_pv<D, true>(s0, s1, vbuf[tl & 1], qc * ksc[tl], col, hi, tail_valid, m, dsum, acc);
+        softmax_pv<D, true>(s0, s1, VfragLds{vbuf[tl & 1], col, hi}, qc * ksc[tl], hi, tail_valid, m, dsum, acc);
     }
 
     const float dt = dsum + shfl_xor_f(dsum, 32);
@@ -556,20 +591,7 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
     const float rinv = 1.0f / dt;
     if (n < p.N) {
         uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
-        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
-#pragma unroll
-        for (int blk = 0; blk < KS; ++blk) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * blk + 8 * r4 + 4 * hi;
-                const float4 sc = *reinterpret_cast<const float4 *>(vs + d0);
-                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc.x;
-                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc.y;
-                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc.z;
-                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc.w;
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-            }
-        }
+        store_o_row<KS>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D, hi, acc, rinv);
     }
     stamp_store(p.stamps, st0);
 }
@@ -872,20 +894,174 @@ __global__ __launch_bounds__(512, 1) void attn_pair256_kernel(const AttnParams p
     const float rinv = 1.0f / dt;
     if (n < p.N) {
         uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh + 128 * hh;
-        const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D + 128 * hh;
+        store_o_row<4>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D + 128 * hh, hi, acc, rinv);
+    }
+    stamp_store(p.stamps, st0);
+}
+
+// ---------------------------------------------------------------------------
+// Segmented schedule inside one work-group (D = 128, short sequences).  The
+// nseg waves of a work-group hold the same 32 query rows; wave s runs the key
+// tiles [s nk / nseg, (s + 1) nk / nseg) from the initial state with the
+// per-tile arithmetic of the exact kernel, and the work-group then combines
+// the segments' (m, d, RO) through LDS in increasing s with the arithmetic
+// and order of attn_seg_combine_kernel: one launch and no partials in HBM,
+// the bytes of the two-launch segmented schedule.
+//
+// Each wave owns a 16 KiB LDS region (K tile, then V tile, in the swizzled
+// layouts of k_lds / v_lds) that only it copies into and reads, so no
+// barrier orders the copies: the wave's own vmcnt says when a copy has
+// landed.  The copies of tile t + 1 go out as soon as the reads of tile t
+// from the same buffer have returned (K after QK, V after PV).
+// ---------------------------------------------------------------------------
+constexpr int kSegWgMax = 8;
+constexpr int kSegWgRegion = 16384;             // LDS bytes per wave
+
+// Waits on the wave's own counters, written as assembly with a memory
+// clobber so that the compiler moves no LDS access across them.
+__device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnParams p) {
+    constexpr int D = 128, KS = D / 32, KT = 64 * D;
+    extern __shared__ __attribute__((aligned(16))) uint8_t segwg_lds[];
+    __shared__ float2 md_s[kSegWgMax][32];
+
+    const Stamp st0 = stamp_now(p.stamps);
+    const int tid = threadIdx.x, lane = tid & 63, seg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5, col = lane & 31;
+    const int nseg = p.nseg;
+
+    const int total = gridDim.x, nxcd = 8;
+    const int xq = total / nxcd, xr = total % nxcd;
+    const int x = blockIdx.x % nxcd, k = blockIdx.x / nxcd;
+    const int lid = x * xq + min(x, xr) + k;
+    const int nqb = (p.N + 31) / 32;                 // 32-row query blocks
+    const int qb = lid % nqb, h = (lid / nqb) % p.Hq, b = lid / (nqb * p.Hq);
+    const int hk = h / p.grp;
+    const int q0 = 32 * qb;
+
+    const int8_t *qrow = p.q8 + (((int64_t)b * p.Hq + h) * p.q_rows + q0 + col) * D + 16 * hi;
+    v4i qf[KS];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const v4i *>(qrow + 32 * s);
+    const float qc = p.q_scale[((int64_t)b * p.Hq + h) * p.nq + qb] * p.c;
+
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(p.k8) + ((int64_t)b * p.Hkv + hk) * p.k_rows * D;
+    const uint8_t *vbase = p.v8 + ((int64_t)b * p.Hkv + hk) * (int64_t)p.nk * KT;
+    // K scales through the scalar cache (wave-uniform), so that waiting for
+    // one does not wait for the copies in flight
+    typedef const float __attribute__((address_space(4))) *kscale_ptr;
+    const kscale_ptr ksc_s = (kscale_ptr)(uintptr_t)(p.k_scale + ((int64_t)b * p.Hkv + hk) * p.nk);
+    const int t0 = (int)((int64_t)seg * p.nk / nseg), t1 = (int)((int64_t)(seg + 1) * p.nk / nseg);
+    const int tail_valid = p.N - 64 * (p.nk - 1);
+
+    uint8_t *region = segwg_lds + seg * kSegWgRegion;
+    const uint8_t *kt = region, *vt = region + KT;
+    const uint32_t kl = lds_addr(region), vl = kl + KT;
+    // source offsets of the lane's chunk in each 1 KiB block j (0..3) of a
+    // tile; blocks 4..7 repeat them 4 KiB further on
+    DmaLane dl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dl[j] = dma_lane(j, lane);
+    auto copy_k = [&](int t) {
+        const uint8_t *src = kbase + (int64_t)t * KT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lds_dma16(src, dl[j].k, kl + 1024 * j);
+            lds_dma16(src + 4096, dl[j].k, kl + 4096 + 1024 * j);
+        }
+    };
+    auto copy_v = [&](int t) {
+        const uint8_t *src = vbase + (int64_t)t * KT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lds_dma16(src, dl[j].v, vl + 1024 * j);
+            lds_dma16(src + 4096, dl[j].v, vl + 4096 + 1024 * j);
+        }
+    };
+
+    v16f acc[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) acc[i] = v16f{};
+    float m = -5000000.0f;
+    float dsum = hi ? 0.0f : 1.0f;
+    // one tile; in flight on entry: the copies of K(t), then of V(t)
+    auto step = [&](int t, auto tail) {
+        wait_vm8();                                                // K(t) landed
+        v16i s0, s1;
+        qk_tile<D>(kt, qf, col, hi, s0, s1);
+        wait_lgkm0();                                              // K(t) read
+        const bool more = t + 1 < t1;
+        if (more) copy_k(t + 1);
+        const float f = qc * ksc_s[t];
+        if (more)                                                  // V(t) landed
+            wait_vm8();
+        else
+            wait_vm0();
+        if constexpr (decltype(tail)::value)
+            softmax_pv<D, true>(s0, s1, VfragLds{vt, col, hi}, f, hi, tail_valid, m, dsum, acc);
+        else
+            softmax_pv<D, false>(s0, s1, VfragLds{vt, col, hi}, f, hi, 64, m, dsum, acc);
+        wait_lgkm0();                                              // V(t) read
+        if (more) copy_v(t + 1);
+    };
+    const bool has_tail = t1 == p.nk && t0 < t1 && tail_valid < 64;
+    const int tend = has_tail ? t1 - 1 : t1;
+    if (t0 < t1) {
+        copy_k(t0);
+        copy_v(t0);
+    }
+    for (int t = t0; t < tend; ++t) step(t, std::false_type{});
+    if (has_tail) step(t1 - 1, std::true_type{});
+    wait_vm0();
+
+    const float dt = dsum + shfl_xor_f(dsum, 32);
+    if (seg > 0) {
+        // the segment's RO into its own region as [blk][r4][lane] float4
+        float4 *ro_w = reinterpret_cast<float4 *>(region);
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                ro_w[(blk * 4 + r4) * 64 + lane] =
+                    make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
+        if (hi == 0) md_s[seg][col] = make_float2(m, dt);
+    }
+    __syncthreads();
+    if (seg > 0) return;
+    // combine in increasing segment order: M = max m_s, a_s = exp2(m_s - M),
+    // d = sum d_s a_s, RO = sum RO_s a_s (from 0)
+    float M = __builtin_fmaxf(-INFINITY, m);
+    for (int s = 1; s < nseg; ++s) M = __builtin_fmaxf(M, md_s[s][col].x);
+    const float a0 = __builtin_amdgcn_exp2f(m - M);
+    float d = 0.0f + dt * a0;
+#pragma unroll
+    for (int blk = 0; blk < KS; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[blk][i] = 0.0f + acc[blk][i] * a0;
+    for (int s = 1; s < nseg; ++s) {
+        const float2 md = md_s[s][col];
+        const float a = __builtin_amdgcn_exp2f(md.x - M);
+        d = d + md.y * a;
+        const float4 *ro_r = reinterpret_cast<const float4 *>(segwg_lds + s * kSegWgRegion);
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * blk + 8 * r4 + 4 * hi;
-                const float4 sc4 = *reinterpret_cast<const float4 *>(vs + d0);
-                const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc4.x;
-                const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc4.y;
-                const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc4.z;
-                const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc4.w;
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                const float4 v = ro_r[(blk * 4 + r4) * 64 + lane];
+                acc[blk][4 * r4 + 0] = acc[blk][4 * r4 + 0] + v.x * a;
+                acc[blk][4 * r4 + 1] = acc[blk][4 * r4 + 1] + v.y * a;
+                acc[blk][4 * r4 + 2] = acc[blk][4 * r4 + 2] + v.z * a;
+                acc[blk][4 * r4 + 3] = acc[blk][4 * r4 + 3] + v.w * a;
             }
-        }
+    }
+    const float rinv = 1.0f / d;
+    const int n = q0 + col;
+    if (n < p.N) {
+        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
+        store_o_row<KS>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D, hi, acc, rinv);
     }
     stamp_store(p.stamps, st0);
 }
@@ -940,6 +1116,30 @@ hipError_t sage_launch_attn(const sage::AttnParams &p, int D, hipStream_t s) {
 }
 
 hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStream_t s) {
+    // short sequences with few segments: one launch, segments combined in LDS
+    // (the same bytes as the two-launch form below)
+    const int64_t nqb32 = (p.N + 31) / 32;
+    if (D == 128 && p.nseg <= sage::kSegWgMax && p.nk <= 64 && nqb32 * p.Hq * p.B <= 2147483647LL) {
+        const unsigned nqb = (unsigned)nqb32;
+        const size_t lds = (size_t)p.nseg * sage::kSegWgRegion;
+        if (lds > 65536) {
+            // dynamic LDS beyond 64 KiB is opted into once per device
+            static std::atomic<bool> opted[64];
+            int dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return e;
+            if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+            if (!opted[dev].load(std::memory_order_acquire)) {
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sage::attn_segwg_kernel),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        sage::kSegWgMax * sage::kSegWgRegion);
+                if (e != hipSuccess) return e;
+                opted[dev].store(true, std::memory_order_release);
+            }
+        }
+        sage::attn_segwg_kernel<<<dim3(nqb * p.Hq * p.B), 64 * p.nseg, lds, s>>>(p);
+        return hipGetLastError();
+    }
     if (D == 128) {
         const unsigned nqt = (unsigned)((p.N + 127) / 128);
         sage::attn_ilv_kernel<128, true><<<dim3(nqt * p.nseg * p.Hq * p.B), 256, 0, s>>>(p);

@@ -45,7 +45,7 @@ def test_segmented_matches_oracle(name, nseg):
     _check(workloads.make_inputs(workloads.CONFIGS[name]), nseg, name)
 
 
-@pytest.mark.parametrize("layer,nseg", [(0, 2), (13, 6), (26, 12)])
+@pytest.mark.parametrize("layer,nseg", [(0, 2), (5, 4), (13, 6), (20, 8), (26, 12)])
 def test_segmented_encoder_layer(layer, nseg):
     cfg = workloads.CONFIGS["encoder"]
     _check(workloads.make_inputs(cfg, layer=layer), nseg, f"encoder layer {layer}")
@@ -64,7 +64,7 @@ def test_segmented_gqa_d256_sampled_rows(nseg):
     _check(inp, nseg, "gqa D=256", rows=rows)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tail"])
+@pytest.mark.parametrize("name", ["tiny", "tail", "encoder"])
 def test_one_segment_is_the_exact_path(name):
     import quantized_exact_order_amd as sage
     inp = workloads.make_inputs(workloads.CONFIGS[name])
@@ -85,7 +85,15 @@ def test_one_segment_is_the_exact_path_d256():
     assert torch.equal(o.view(torch.int16), o1.view(torch.int16))
 
 
-@pytest.mark.parametrize("N,nseg", [(1, 1), (65, 2), (129, 3), (300, 5)])
+@pytest.mark.parametrize("nseg", [3, 7])
+def test_segmented_long_d128_sampled_rows(nseg):
+    # more than 64 key tiles: the two-launch form (partials, then combine)
+    inp = workloads.make_custom(1, 4200, 2, 2, 128, 96, seed=31)
+    rows = np.array([(0, h, i) for h in range(2) for i in (0, 31, 32, 2047, 4100, 4199)], np.int32)
+    _check(inp, nseg, "d128 N=4200", rows=rows)
+
+
+@pytest.mark.parametrize("N,nseg", [(1, 1), (33, 1), (65, 2), (129, 3), (300, 5), (700, 8)])
 def test_segmented_small_and_ragged_lengths(N, nseg):
     inp = workloads.make_inputs(workloads.CONFIGS["tiny"], N=N)
     _check(inp, nseg, f"tiny N={N}")

@@ -166,29 +166,39 @@ __device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const
         acc[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vfrag(blk), pb, acc[blk], 0, 0, 0, 0, 0, 0);
 }
 
-// Final BF16 row of the lane's query: O = (RO / d) x V scale for channels
-// 32 blk + 8 r4 + 4 hi + 0..3.  All the V-scale loads go out before the first
-// store, so the wave waits for them once (a store between two loads would
-// make each load wait for the store ahead of it).
-template <int NB>
-__device__ __forceinline__ void store_o_row(uint16_t *orow, const float *vs, int hi, const v16f (&acc)[NB],
-                                            float rinv) {
-    float4 sc[NB][4];
+// Writes a wave's 32 x 128 block of the BF16 output, O = (RO / d) x V scale,
+// with whole 256-byte row segments.  The lane holds row col, channels
+// 32 blk + 8 r4 + 4 hi + 0..3; its values go to an 8 KiB LDS stage that only
+// this wave uses (16-byte chunks XOR-swizzled by row, against bank
+// conflicts), and 16 lanes then store each row.  All V-scale loads go out
+// before the first store: a store between two loads would make each load
+// wait for the store ahead of it.  o0 points at the block's first row and
+// channel; rows >= nvalid are not written.
+__device__ __forceinline__ void store_o_block(uint16_t *o0, int64_t osn, int nvalid, uint8_t *stage,
+                                              const float *vs, int lane, const v16f (&acc)[4], float rinv) {
+    const int hi = lane >> 5, col = lane & 31;
+    float4 sc[4][4];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) sc[blk][r4] = *reinterpret_cast<const float4 *>(vs + 32 * blk + 8 * r4 + 4 * hi);
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
+    for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int d0 = 32 * blk + 8 * r4 + 4 * hi;
-            const float o0 = (acc[blk][4 * r4 + 0] * rinv) * sc[blk][r4].x;
-            const float o1 = (acc[blk][4 * r4 + 1] * rinv) * sc[blk][r4].y;
-            const float o2 = (acc[blk][4 * r4 + 2] * rinv) * sc[blk][r4].z;
-            const float o3 = (acc[blk][4 * r4 + 3] * rinv) * sc[blk][r4].w;
-            *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            const float o_0 = (acc[blk][4 * r4 + 0] * rinv) * sc[blk][r4].x;
+            const float o_1 = (acc[blk][4 * r4 + 1] * rinv) * sc[blk][r4].y;
+            const float o_2 = (acc[blk][4 * r4 + 2] * rinv) * sc[blk][r4].z;
+            const float o_3 = (acc[blk][4 * r4 + 3] * rinv) * sc[blk][r4].w;
+            *reinterpret_cast<uint2 *>(stage + col * 256 + 16 * ((4 * blk + r4) ^ (col & 15)) + 8 * hi) =
+                make_uint2(pack_bf16x2(o_0, o_1), pack_bf16x2(o_2, o_3));
         }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), c = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (c ^ (r & 15)));
+        if (r < nvalid) *reinterpret_cast<uint4 *>(o0 + r * osn + 8 * c) = v;
     }
 }
 
@@ -589,10 +599,10 @@ __global__ __launch_bounds__(256, 2) void attn_ilv_kernel(const AttnParams p) {
         return;
     }
     const float rinv = 1.0f / dt;
-    if (n < p.N) {
-        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
-        store_o_row<KS>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D, hi, acc, rinv);
-    }
+    __syncthreads();                                 // the tile buffers are free: output stage
+    store_o_block(p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh, p.osn, p.N - q0,
+                  wave < 2 ? kbuf[wave] : vbuf[wave - 2], p.v_scale + ((int64_t)b * p.Hkv + hk) * D, lane, acc,
+                  rinv);
     stamp_store(p.stamps, st0);
 }
 
@@ -892,10 +902,10 @@ __global__ __launch_bounds__(512, 1) void attn_pair256_kernel(const AttnParams p
         return;
     }
     const float rinv = 1.0f / dt;
-    if (n < p.N) {
-        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh + 128 * hh;
-        store_o_row<4>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D + 128 * hh, hi, acc, rinv);
-    }
+    // the barrier above also ended every read of the tile buffers: output stage
+    store_o_block(p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh + 128 * hh, p.osn, p.N - q0,
+                  wave < 4 ? kbuf[0] + 8192 * wave : vbuf[0] + 8192 * (wave - 4),
+                  p.v_scale + ((int64_t)b * p.Hkv + hk) * D + 128 * hh, lane, acc, rinv);
     stamp_store(p.stamps, st0);
 }
 
@@ -1058,11 +1068,9 @@ __global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnPa
             }
     }
     const float rinv = 1.0f / d;
-    const int n = q0 + col;
-    if (n < p.N) {
-        uint16_t *orow = p.o + (int64_t)b * p.osb + (int64_t)n * p.osn + (int64_t)h * p.osh;
-        store_o_row<KS>(orow, p.v_scale + ((int64_t)b * p.Hkv + hk) * D, hi, acc, rinv);
-    }
+    // wave 0's own region (its tiles are done) is the output stage
+    store_o_block(p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh, p.osn, p.N - q0, segwg_lds,
+                  p.v_scale + ((int64_t)b * p.Hkv + hk) * D, lane, acc, rinv);
     stamp_store(p.stamps, st0);
 }
 

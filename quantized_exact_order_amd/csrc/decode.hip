@@ -192,8 +192,7 @@ struct KStep {
     float4 k0, k1;
 };
 
-__device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const float *ksb, int ts, int T,
-                                            int q4, int r16) {
+__device__ __forceinline__ void load_k_rows(KStep &k, const int8_t *kb, int ts, int T, int q4, int r16) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
         const int tok = min(ts + 8 * (r16 >> 2) + 4 * bb + (r16 & 3), T - 1);
@@ -201,6 +200,8 @@ __device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const fl
 #pragma unroll
         for (int s = 0; s < 4; ++s) k.a[bb][s] = *reinterpret_cast<const v4i *>(kr + 64 * s);
     }
+}
+__device__ __forceinline__ void load_k_scales(KStep &k, const float *ksb, int ts, int T, int q4) {
     // a group of 8 past T reads the last valid group (its scores are masked);
     // t8 + 8 <= capacity since both are multiples of 8
     const int t8 = min(ts + 8 * q4, ((T - 1) / 8) * 8);
@@ -208,6 +209,11 @@ __device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const fl
     const v4f s1 = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(ksb + t8 + 4));
     k.k0 = make_float4(s0[0], s0[1], s0[2], s0[3]);
     k.k1 = make_float4(s1[0], s1[1], s1[2], s1[3]);
+}
+__device__ __forceinline__ void load_k_step(KStep &k, const int8_t *kb, const float *ksb, int ts, int T,
+                                            int q4, int r16) {
+    load_k_rows(k, kb, ts, T, q4, r16);
+    load_k_scales(k, ksb, ts, T, q4);
 }
 
 // The V block of tokens ts + 8 q4 .. + 7 for channels 16 nb + r16 (the B
@@ -246,7 +252,8 @@ __device__ __forceinline__ void load_v8_step(uint4 vv[16], float4 &s0, float4 &s
 // (integers of magnitude <= 128 have at most 8 significant bits).
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int j) {
     const float a = (float)(int8_t)(w >> (16 * j)), c = (float)(int8_t)(w >> (16 * j + 8));
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(c) & 0xffff0000u);
+    // the high halves of a (bytes 2, 3) and c (bytes 6, 7 of the pair c:a)
+    return __builtin_amdgcn_perm(__float_as_uint(c), __float_as_uint(a), 0x07060302u);
 }
 
 // Chunk partial of the grp (<= 16) query heads of one KV head over tokens
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     __shared__ float wl[4][kDecodeMaxGroup];                                         // per-wave sums
     __shared__ __attribute__((aligned(16))) float osum[kDecodeMaxGroup][260];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q4 = lane >> 4, r16 = lane & 15;
     const int hk = blockIdx.x % p.Hkv, chunk = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int64_t bh = (int64_t)b * p.Hkv + hk;
@@ -298,9 +305,9 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     KStep k;
     uint4 vv[16];
     float4 vs0, vs1;                        // INT8 V: scales of the lane's 8 tokens
+    load_k_step(k, kb, ksb, tw, T, q4, r16);
     if constexpr (kInt8V) load_v8_step(vv, vs0, vs1, vb8, vsb, tw, T, q4, r16);
     else load_v_step(vv, vb, tw, T, q4, r16);
-    load_k_step(k, kb, ksb, tw, T, q4, r16);
     __builtin_amdgcn_sched_barrier(0);      // every load above is issued before the expansion
 
     // rotated queries -> three INT8 parts q_j with scales s_j (s_{j+1} =
@@ -344,14 +351,19 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     v4f o[16];                              // register i: head 4 q4 + i, channel 16 nb + r16
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    // Step st finds in flight, in this order: its K rows, its K scales and
+    // its V.  The K rows of step st + 1 go out once the scores have read this
+    // step's, its K scales once the dequantization has read this step's, and
+    // its V once the PV products have read this step's.  Every step issues
+    // the same loads, so that the compiler's waits count them exactly: on the
+    // last step they are dummies, every lane reading the first row or block
+    // of the step (one cache line per load), and nothing uses them.
 #pragma unroll 1
     for (int st = 0; st < nst; ++st) {
         const int ts = tw + 128 * st;
-        if (st > 0) {
-            if constexpr (kInt8V) load_v8_step(vv, vs0, vs1, vb8, vsb, ts, T, q4, r16);
-            else load_v_step(vv, vb, ts, T, q4, r16);
-            load_k_step(k, kb, ksb, ts, T, q4, r16);
-        }
+        const bool more = st + 1 < nst;
+        const int tn = more ? ts + 128 : ts;
+        const int q4n = more ? q4 : 0, r16n = more ? r16 : 0;
 
         // scores of tokens ts + 8 q4 + e, head r16: B operand (part j, d-step
         // s) = bytes 16 q4 + 64 s .. + 15 of part j of head r16
@@ -368,11 +380,14 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 // volatile: read at its use each step, not hoisted out of the loop
-                const v4i qb = *reinterpret_cast<const volatile v4i *>(&qp[j][r16][16 * q4 + 64 * s]);
+                typedef const volatile v4i __attribute__((address_space(3))) *lds_v4i;
+                const v4i qb = *(lds_v4i)(uintptr_t)(uint32_t)(uintptr_t)&qp[j][r16][16 * q4 + 64 * s];
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb)
                     acc[bb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k.a[bb][s], qb, acc[bb][j], 0, 0, 0);
             }
+        // the next step's K rows into the registers the scores just read
+        load_k_rows(k, kb, tn, T, q4n, r16n);
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -383,6 +398,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
                 x = __builtin_fmaf((float)acc[bb][2][i], s3, x);
                 sc[e] = (t8 + e < T) ? x * (ks[e] * 0.0625f) : -INFINITY;
             }
+        // and its K scales into the registers the dequantization just read
+        load_k_scales(k, ksb, tn, T, q4n);
 
         // online softmax over the step (its first token is valid: mx is finite)
         float mx = sc[0];
@@ -443,6 +460,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, bv, o[nb], 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl8, bv, o[nb], 0, 0, 0);
         }
+        if constexpr (kInt8V) load_v8_step(vv, vs0, vs1, vb8, vsb, tn, T, q4n, r16n);
+        else load_v_step(vv, vb, tn, T, q4n, r16n);
     }
 
     // merge the four waves: M = max_w m_w, o = sum_w o_w e^(m_w - M) in the

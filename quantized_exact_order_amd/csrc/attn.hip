@@ -174,14 +174,17 @@ __device__ __forceinline__ void softmax_pv(const v16i &s0, const v16i &s1, const
 // before the first store: a store between two loads would make each load
 // wait for the store ahead of it.  o0 points at the block's first row and
 // channel; rows >= nvalid are not written.
-__device__ __forceinline__ void store_o_block(uint16_t *o0, int64_t osn, int nvalid, uint8_t *stage,
-                                              const float *vs, int lane, const v16f (&acc)[4], float rinv) {
-    const int hi = lane >> 5, col = lane & 31;
-    float4 sc[4][4];
+__device__ __forceinline__ void load_o_scales(const float *vs, int lane, float4 (&sc)[4][4]) {
+    const int hi = lane >> 5;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) sc[blk][r4] = *reinterpret_cast<const float4 *>(vs + 32 * blk + 8 * r4 + 4 * hi);
+}
+__device__ __forceinline__ void store_o_block(uint16_t *o0, int64_t osn, int nvalid, uint8_t *stage,
+                                              const float4 (&sc)[4][4], int lane, const v16f (&acc)[4],
+                                              float rinv) {
+    const int col = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
@@ -200,6 +203,12 @@ __device__ __forceinline__ void store_o_block(uint16_t *o0, int64_t osn, int nva
         const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 256 + 16 * (c ^ (r & 15)));
         if (r < nvalid) *reinterpret_cast<uint4 *>(o0 + r * osn + 8 * c) = v;
     }
+}
+__device__ __forceinline__ void store_o_block(uint16_t *o0, int64_t osn, int nvalid, uint8_t *stage,
+                                              const float *vs, int lane, const v16f (&acc)[4], float rinv) {
+    float4 sc[4][4];
+    load_o_scales(vs, lane, sc);
+    store_o_block(o0, osn, nvalid, stage, sc, lane, acc, rinv);
 }
 
 // Segmented (split-KV) schedule, an opt-in mode outside the contract's
@@ -1039,22 +1048,32 @@ __global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnPa
                     make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
         if (hi == 0) md_s[seg][col] = make_float2(m, dt);
     }
+    // wave 0: the output's V scales go out before the wait for the others
+    float4 sc[4][4];
+    if (seg == 0) load_o_scales(p.v_scale + ((int64_t)b * p.Hkv + hk) * D, lane, sc);
     __syncthreads();
     if (seg > 0) return;
     // combine in increasing segment order: M = max m_s, a_s = exp2(m_s - M),
     // d = sum d_s a_s, RO = sum RO_s a_s (from 0)
+    float2 mds[kSegWgMax];
+#pragma unroll
+    for (int s = 1; s < kSegWgMax; ++s)
+        if (s < nseg) mds[s] = md_s[s][col];
     float M = __builtin_fmaxf(-INFINITY, m);
-    for (int s = 1; s < nseg; ++s) M = __builtin_fmaxf(M, md_s[s][col].x);
+#pragma unroll
+    for (int s = 1; s < kSegWgMax; ++s)
+        if (s < nseg) M = __builtin_fmaxf(M, mds[s].x);
     const float a0 = __builtin_amdgcn_exp2f(m - M);
     float d = 0.0f + dt * a0;
 #pragma unroll
     for (int blk = 0; blk < KS; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[blk][i] = 0.0f + acc[blk][i] * a0;
-    for (int s = 1; s < nseg; ++s) {
-        const float2 md = md_s[s][col];
-        const float a = __builtin_amdgcn_exp2f(md.x - M);
-        d = d + md.y * a;
+#pragma unroll
+    for (int s = 1; s < kSegWgMax; ++s) {
+        if (s >= nseg) break;
+        const float a = __builtin_amdgcn_exp2f(mds[s].x - M);
+        d = d + mds[s].y * a;
         const float4 *ro_r = reinterpret_cast<const float4 *>(segwg_lds + s * kSegWgRegion);
 #pragma unroll
         for (int blk = 0; blk < KS; ++blk)
@@ -1070,7 +1089,7 @@ __global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnPa
     const float rinv = 1.0f / d;
     // wave 0's own region (its tiles are done) is the output stage
     store_o_block(p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh, p.osn, p.N - q0, segwg_lds,
-                  p.v_scale + ((int64_t)b * p.Hkv + hk) * D, lane, acc, rinv);
+                  sc, lane, acc, rinv);
     stamp_store(p.stamps, st0);
 }
 

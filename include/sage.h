@@ -164,8 +164,10 @@ sage_status sage_attn_fwd(const sage_shape *shape, const sage_bufs *bufs, void *
  * Cycles over wall ticks, times the constant counter's rate
  * (sage_wall_clock_khz), is the shader clock the launch ran at.
  *   stamps       device memory, 16-byte aligned, of at least
- *                sage_attn_stamp_bytes bytes (32 per work-group of
- *                128 query rows: B * Hq * ceil(N/128) of them)
+ *                sage_attn_stamp_bytes bytes (32 for every 32 query rows
+ *                of every head: B * Hq * ceil(N/32) records, at least one
+ *                per work-group of any launch; records past the launch's
+ *                work-groups are not written)
  * Refusals: those of sage_attn_fwd, SAGE_E_NULL, SAGE_E_WORKSPACE (stamps
  * too small), SAGE_E_ALIGN. */
 sage_status sage_attn_stamp_bytes(const sage_shape *shape, size_t *bytes);

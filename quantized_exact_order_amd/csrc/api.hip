@@ -185,8 +185,8 @@ sage_status check_nseg(const sage_shape *shape, int32_t nseg) {
     sage_sizes z;
     fill_sizes(shape, &z);
     if (nseg < 1 || nseg > z.n_k_tiles) return SAGE_E_SHAPE;
-    const int64_t nqt = (shape->N + 127) / 128;                    // 128 query rows per work-group
-    if (nqt * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
+    const int64_t nqb = (shape->N + 31) / 32;                      // at least 32 query rows per work-group
+    if (nqb * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
     if (seg_ro_bytes(shape, nseg) == 0) return SAGE_E_SHAPE;
     return SAGE_OK;
 }
@@ -205,7 +205,9 @@ sage_status sage_attn_stamp_bytes(const sage_shape *shape, size_t *bytes) {
     sage_status st = check_shape(shape);
     if (st != SAGE_OK) return st;
     if (!bytes) return SAGE_E_NULL;
-    *bytes = (size_t)shape->B * shape->Hq * (size_t)((shape->N + 127) / 128) * 4 * sizeof(uint64_t);
+    // one record per work-group; no launch has more than one work-group per
+    // 32 query rows of a head
+    *bytes = (size_t)shape->B * shape->Hq * (size_t)((shape->N + 31) / 32) * 4 * sizeof(uint64_t);
     return SAGE_OK;
 }
 

@@ -185,8 +185,10 @@ sage_status check_nseg(const sage_shape *shape, int32_t nseg) {
     sage_sizes z;
     fill_sizes(shape, &z);
     if (nseg < 1 || nseg > z.n_k_tiles) return SAGE_E_SHAPE;
-    const int64_t nqb = (shape->N + 31) / 32;                      // at least 32 query rows per work-group
-    if (nqb * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
+    // the two-launch form: 128 query rows per work-group and segment (the
+    // one-work-group form checks its own grid and otherwise takes this one)
+    const int64_t nqt = (shape->N + 127) / 128;
+    if (nqt * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
     if (seg_ro_bytes(shape, nseg) == 0) return SAGE_E_SHAPE;
     return SAGE_OK;
 }

@@ -32,6 +32,7 @@
 // normalized transform (its own inverse) to the output before rounding.
 
 #include "decode.h"
+#include "lanes.h"
 
 #include <mutex>
 
@@ -50,15 +51,15 @@ __device__ __forceinline__ void wht256(float u[4], int lane) {
     u[0] = a + b; u[2] = a - b;
     a = u[1]; b = u[3];
     u[1] = a + b; u[3] = a - b;
-#pragma unroll
-    for (int lm = 1; lm < 64; lm <<= 1) {
+    for_pow2<1, 64>([&](auto m) {
+        constexpr int lm = decltype(m)::value;
         const bool upper = (lane & lm) != 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float other = shfl_xor_f(u[i], lm);
+            const float other = xor_lane<lm>(u[i]);
             u[i] = upper ? (other - u[i]) : (u[i] + other);
         }
-    }
+    });
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = u[i] * 0.0625f;
 }
@@ -81,7 +82,7 @@ __device__ __forceinline__ uint32_t rot_quant_row(const uint16_t *row, int lane,
     wht256(u, lane);
     float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
                               __builtin_fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
-    m = wave_max_f(m);
+    m = wave_max_x(m);
     amax = (m > 1e-7f) ? m : 1e-7f;
     const float mul = 127.0f / amax;
     uint32_t w = 0;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
         wht256(x, lane);
         float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
                                   __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
-        a = wave_max_f(a);
+        a = wave_max_x(a);
         float sc = a / 127.0f, mu = 127.0f / a;
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -405,8 +406,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
         float mx = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = __builtin_fmaxf(mx, sc[e]);
-        mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = __builtin_fmaxf(mx, shfl_xor_f(mx, 32));
+        mx = __builtin_fmaxf(mx, xor_lane<16>(mx));
+        mx = __builtin_fmaxf(mx, xor_lane<32>(mx));
         const float mn = __builtin_fmaxf(m, mx);
         const float alpha = expf(m - mn);                   // 0 on the first step
         l = l * alpha;
@@ -467,8 +468,8 @@ __global__ __launch_bounds__(256, 2) void decode_chunk_kernel(const DecodeParams
     // merge the four waves: M = max_w m_w, o = sum_w o_w e^(m_w - M) in the
     // order 0, 1, 2, 3 (wave 0 starts at the chunk's first token, which is
     // valid; a wave with no tokens has m = -inf and adds zero)
-    l = l + shfl_xor_f(l, 16);
-    l = l + shfl_xor_f(l, 32);
+    l = l + xor_lane<16>(l);
+    l = l + xor_lane<32>(l);
     if (q4 == 0) {
         wm[wave][r16] = m;
         wl[wave][r16] = l;
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
     float M = mc;
     for (int c = tid + kCombineThreads; c < nchunk; c += kCombineThreads)
         M = __builtin_fmaxf(M, src[(int64_t)c * kPartStride + 256]);
-    M = wave_max_f(M);
+    M = wave_max_x(M);
     if (lane == 0) wmax[wave] = M;
     __syncthreads();
     M = wmax[0];

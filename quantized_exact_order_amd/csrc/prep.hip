@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "device.h"
+#include "lanes.h"
 
 namespace sage {
 namespace {
@@ -98,8 +99,7 @@ __device__ __forceinline__ uint4 rmsnorm8(const float x[8], const float wv[8], f
     float a0 = t[0] + t[1], a1 = t[2] + t[3], a2 = t[4] + t[5], a3 = t[6] + t[7];
     float b0 = a0 + a1, b1 = a2 + a3;
     float ss = b0 + b1;
-#pragma unroll
-    for (int m = 1; m < L; m <<= 1) ss = ss + shfl_xor_f(ss, m);
+    for_pow2<1, L>([&](auto m) { ss = ss + xor_lane<decltype(m)::value>(ss); });
     float inv = 1.0f / sqrtf(ss / (float)D + eps);
     float n2[8];
 #pragma unroll
@@ -182,15 +182,15 @@ __device__ __forceinline__ void wht8(float u[8], int j) {
             }
         }
     }
-#pragma unroll
-    for (int lm = 1; lm < L; lm <<= 1) {
+    for_pow2<1, L>([&](auto m) {
+        constexpr int lm = decltype(m)::value;
         const bool upper = (j & lm) != 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float other = shfl_xor_f(u[i], lm);
+            const float other = xor_lane<lm>(u[i]);
             u[i] = upper ? (other - u[i]) : (u[i] + other);
         }
-    }
+    });
     const float s = (L == 32) ? 0.0625f : 1.0f / sqrtf((float)(8 * L));
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = u[i] * s;
@@ -419,11 +419,14 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
     const int g = (blockIdx.x / p.Hq) * 4 + wave;
     uint16_t *yb = ybuf[wave];
 
-    // every row load of the wave first, then the RoPE coefficients (all of
-    // them when they fit in registers, else each at its pass)
+    // every row load of the wave first, then the RoPE coefficients: all of
+    // them when they fit in registers, else in groups of CG passes, each
+    // group's loads issued together ahead of its passes (a load per pass,
+    // next to a store that may alias it, would cost a round trip per pass)
     constexpr bool PRE = NP <= 8;
+    constexpr int CG = PRE ? NP : 4;
     uint4 qraw[NP];
-    Coef8 cf[PRE ? NP : 1];
+    Coef8 cf[CG];
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int n = 32 * g + pass * RPW + rr;
@@ -446,7 +449,16 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
     for (int pass = 0; pass < NP; ++pass) {
         const int r = pass * RPW + rr, n = 32 * g + r;
         const int nc = n < p.N ? n : 0;
-        const Coef8 k = PRE ? cf[PRE ? pass : 0] : rope_coef8(p.cos_t, p.sin_t, nc, j, p.R);
+        if constexpr (!PRE) {
+            if (pass % CG == 0) {
+#pragma unroll
+                for (int i = 0; i < CG; ++i) {
+                    const int ni = 32 * g + (pass + i) * RPW + rr;
+                    cf[i] = rope_coef8(p.cos_t, p.sin_t, ni < p.N ? ni : 0, j, p.R);
+                }
+            }
+        }
+        const Coef8 k = cf[pass % CG];
         rope8(&yb[r * D], j, nc, p.R, p.cos_t, p.sin_t, k, u[pass]);
         if (p.q_prep && n < p.N)
             *reinterpret_cast<uint4 *>(p.q_prep + (((int64_t)b * p.Hq + h) * p.N + n) * D + 8 * j) = pack8(u[pass]);
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
             for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(u[pass][i]));
         }
     }
-    amax = wave_max_f(amax);
+    amax = wave_max_x(amax);
     amax = (amax > 1e-7f) ? amax : 1e-7f;
     const float scale = amax / 127.0f;
     const float mul = 127.0f / amax;
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
             for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(u[pass][i]));
         }
     }
-    amax = wave_max_f(amax);
+    amax = wave_max_x(amax);
     if ((tid & 63) == 0) wmax[tid >> 6] = amax;
     __syncthreads();
     amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));

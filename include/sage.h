@@ -305,12 +305,17 @@ size_t sage_decode_noalloc_max_bytes(void);
  *   kind 9  OCP E4M3 as the V cast converts (hardware  uint8  [count]
  *           conversion; equal to kind 2 for |x| < 448
  *           and NaN; the V cast's values stay below 2.25)
+ *   kind 10..15  the lane exchange of the preparation   float  [count]
+ *           and decode reductions and butterflies at
+ *           xor distance M = 2^(kind - 10): element i
+ *           gets the input of element i ^ M (i within
+ *           its wave of 64; count a multiple of 64)
  * For tests that compare these roundings with an independent implementation
  * over every FP32 pattern (Preparation; Q And K Quantization; V And PV), and
  * that measure the accuracy of the softmax exponential (Online Softmax).
  * Refusals: SAGE_E_NULL, SAGE_E_ALIGN, SAGE_E_UNSUPPORTED (kind outside
- * 0..9), SAGE_E_SHAPE (count < 1, count > 2^26, or first + count > 2^32),
- * SAGE_E_HIP. */
+ * 0..15), SAGE_E_SHAPE (count < 1, count > 2^26, first + count > 2^32, or
+ * for kinds 10..15 a count that is not a multiple of 64), SAGE_E_HIP. */
 sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream);
 
 /* Key (0..63, within its tile) stored at position `slot` (0..63) of every

@@ -258,7 +258,8 @@ _PRIMITIVE_DTYPES = {0: torch.int16, 1: torch.int8, 2: torch.uint8, 9: torch.uin
 def selftest_primitive(kind: int, first: int, count: int, out: Optional[torch.Tensor] = None,
                        stream=None) -> torch.Tensor:
     """Test hook (sage_selftest_primitive): device number-format primitive
-    `kind` (0 BF16 bits as int16, 1 INT8, 2 and 9 E4M3 bytes, 3..8 FP32 results) of
+    `kind` (0 BF16 bits as int16, 1 INT8, 2 and 9 E4M3 bytes, 3..8 FP32 results,
+    10..15 the lane exchange at xor distance 2^(kind-10), FP32 bits moved) of
     the FP32 values with bit patterns first .. first + count - 1."""
     dt = _PRIMITIVE_DTYPES.get(kind, torch.float32)
     if out is None:

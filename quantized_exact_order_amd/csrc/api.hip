@@ -370,8 +370,9 @@ size_t sage_decode_noalloc_max_bytes(void) { return sage::kDecodeScratchBytes; }
 sage_status sage_selftest_primitive(int32_t kind, uint32_t first, uint32_t count, void *out, void *stream) {
     if (!out) return SAGE_E_NULL;
     if (!aligned16(out)) return SAGE_E_ALIGN;
-    if (kind < 0 || kind > 9) return SAGE_E_UNSUPPORTED;
+    if (kind < 0 || kind > 15) return SAGE_E_UNSUPPORTED;
     if (count < 1 || count > (1u << 26) || (uint64_t)first + count > (uint64_t(1) << 32)) return SAGE_E_SHAPE;
+    if (kind >= 10 && count % 64 != 0) return SAGE_E_SHAPE;            // lane exchanges: whole waves
     return sage_launch_primitive(kind, first, count, out, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGE_OK
                                                                                                         : SAGE_E_HIP;
 }

@@ -11,12 +11,15 @@
 
 namespace sage {
 
-// The value that lane l ^ M holds (M a power of two below 64):
-//   M = 1, 2:      DPP quad permutation (v_mov_b32_dpp);
-//   M = 4, 8, 16:  ds_swizzle_b32 in bitmask mode (within groups of 32 lanes:
-//                  and-mask 0x1F, or-mask 0, xor-mask M), no LDS access;
-//   M = 32:        v_permlane32_swap, which returns the upper half's values
-//                  to the lower half and the lower half's to the upper one.
+// The value that lane l ^ M holds (M a power of two below 64), all by VALU
+// lane moves:
+//   M = 1, 2:  DPP quad permutation (v_mov_b32_dpp quad_perm);
+//   M = 4:     DPP row_half_mirror (l -> l ^ 7 within 8 lanes), then quad_perm
+//              [3, 2, 1, 0] (l -> l ^ 3 within 4);
+//   M = 8:     DPP row_ror:8 (a rotation by 8 within 16 lanes is l ^ 8);
+//   M = 16:    v_permlane16_swap, M = 32: v_permlane32_swap; each returns the
+//              partner rows' values to one half of the lanes in its first
+//              result and to the other half in its second.
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
     static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "xor distance");
@@ -26,11 +29,17 @@ __device__ __forceinline__ float xor_lane(float v) {
         r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);          // quad_perm [1, 0, 3, 2]
     } else if constexpr (M == 2) {
         r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);          // quad_perm [2, 3, 0, 1]
-    } else if constexpr (M == 32) {
+    } else if constexpr (M == 4) {
+        const int hm = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        r = __builtin_amdgcn_mov_dpp(hm, 0x1B, 0xF, 0xF, false);          // quad_perm [3, 2, 1, 0]
+    } else if constexpr (M == 8) {
+        r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);         // row_ror:8
+    } else if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        r = (threadIdx.x & 16) ? (int)p[0] : (int)p[1];
+    } else {
         const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
         r = (threadIdx.x & 32) ? (int)p[0] : (int)p[1];
-    } else {
-        r = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
     }
     return __int_as_float(r);
 }

@@ -18,8 +18,14 @@
 //      (not a bit-exact output: its accuracy is measured, not pinned)
 //   9  OCP E4M3 as the V cast converts (pack4_e4m3_bounded) -> uint8
 //      (equal to kind 2 for NaN and below 448 in magnitude)
+//  10..15  the lane exchange of the row reductions and butterflies
+//      (xor_lane<M>, M = 2^(kind - 10)): element i receives the input of
+//      element i ^ M of its wave (a data move: the bits come through as
+//      they are)                                       -> float bits
+// The exchange kinds need whole waves: count a multiple of 64.
 
 #include "device.h"
+#include "lanes.h"
 
 namespace sage {
 namespace {
@@ -42,6 +48,12 @@ __global__ __launch_bounds__(256) void primitive_kernel(int kind, uint32_t first
         static_cast<uint8_t *>(out)[i] = (uint8_t)(pack4_e4m3_bounded(v) & 0xffu);
         break;
     }
+    case 10: static_cast<float *>(out)[i] = xor_lane<1>(x); break;
+    case 11: static_cast<float *>(out)[i] = xor_lane<2>(x); break;
+    case 12: static_cast<float *>(out)[i] = xor_lane<4>(x); break;
+    case 13: static_cast<float *>(out)[i] = xor_lane<8>(x); break;
+    case 14: static_cast<float *>(out)[i] = xor_lane<16>(x); break;
+    case 15: static_cast<float *>(out)[i] = xor_lane<32>(x); break;
     default: static_cast<float *>(out)[i] = __builtin_amdgcn_exp2f(x); break;
     }
 }

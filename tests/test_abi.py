@@ -207,7 +207,8 @@ def test_primitive_hook_refusals_happen_before_launch(sage):
     assert prim(0, 0, 16, out=None) == "SAGE_E_NULL"
     assert prim(0, 0, 16, out=A + 4) == "SAGE_E_ALIGN"
     assert prim(-1, 0, 16) == "SAGE_E_UNSUPPORTED"
-    assert prim(10, 0, 16) == "SAGE_E_UNSUPPORTED"
+    assert prim(16, 0, 16) == "SAGE_E_UNSUPPORTED"
+    assert prim(10, 0, 96) == "SAGE_E_SHAPE"                        # lane exchanges take whole waves
     assert prim(0, 0, 0) == "SAGE_E_SHAPE"
     assert prim(0, 0, (1 << 26) + 1) == "SAGE_E_SHAPE"             # more than one chunk
     assert prim(0, 0xFFFFFFF0, 17) == "SAGE_E_SHAPE"                # runs past pattern 2^32 - 1

@@ -10,7 +10,9 @@
   squares and maxima), against numpy's correctly rounded float32 division
   and square root;
 - the accuracy of the softmax exponential (not a bit-exact output) over every
-  argument from -126 to 8.81, against FP64.
+  argument from -126 to 8.81, against FP64;
+- the lane exchanges of the preparation and decode reductions (DPP, permlane
+  moves): element i of every wave receives element i ^ M, bits unchanged.
 
 Results must be bit-identical; where both sides give NaN the payloads are not
 compared."""
@@ -137,3 +139,17 @@ def test_softmax_exponential_accuracy():
     print(f"[gpu] v_exp_f32: max error {w_pos:.3f} ulp at x = {x_pos!r} (x >= 0), {w_neg:.3f} ulp at "
           f"x = {x_neg!r} (x < 0)", flush=True)
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("kind", range(10, 16))
+def test_lane_exchange_moves_the_partner_lanes_bits(kind):
+    # patterns around 1.0, and a range of NaN payloads: a move keeps every bit
+    import quantized_exact_order_amd as sage
+    m = 1 << (kind - 10)
+    banner(f"lane exchange xor {m}")
+    for first in (0x3F800000, 0x7FC00000 - 2048, 0xFF800000 - 4096):
+        n = 8192
+        out = sage.selftest_primitive(kind, first, n).view(torch.int32).cpu().numpy().view(np.uint32)
+        i = np.arange(n, dtype=np.uint64)
+        want = (np.uint64(first) + (i ^ np.uint64(m))).astype(np.uint32)
+        assert np.array_equal(out, want), (m, hex(first), int(np.count_nonzero(out != want)))

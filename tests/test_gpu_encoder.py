@@ -96,3 +96,23 @@ def test_hip_graph_replays_match_eager():
             for name, t in host_tensors(one, b).items():
                 assert np.array_equal(t.view(np.uint8), eager_tensors[l][name].view(np.uint8)), \
                     f"replay {rep} layer {l} {name}"
+
+
+@pytest.mark.parametrize("nseg", [2, 4, 12])
+def test_stacked_segmented_equals_per_layer_segmented(nseg):
+    # the segmented mode keeps every (batch, head, query block) on its own,
+    # so stacking layers along the batch must not change a byte of any layer
+    # (nseg 2 and 4 run in one work-group, 12 in two launches)
+    import quantized_exact_order_amd as sage
+    n = 3
+    banner(f"encoder: {n} layers stacked vs single calls, segmented nseg={nseg}")
+    cfg, layers, q, k, v, extra = _stacked_inputs(n, "cuda")
+    one, bufs1, _ = _per_layer(sage, cfg, q, k, v, extra, n)
+    o1 = torch.stack([sage.attn_fwd_segmented(one, bufs1[l], nseg)[0] for l in range(n)])
+    stacked = sage.Shape(n, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.rope_dim, cfg.hadamard, cfg.eps)
+    bufsL = sage.Buffers.allocate(stacked, q.device)
+    sage.prep(stacked, bufsL, q, k, v, *extra)
+    sage.quant_qk(stacked, bufsL, q, k, v, *extra)
+    oL = sage.attn_fwd_segmented(stacked, bufsL, nseg)
+    torch.cuda.synchronize()
+    assert torch.equal(oL.view(torch.int16), o1.view(torch.int16))

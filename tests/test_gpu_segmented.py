@@ -93,6 +93,14 @@ def test_segmented_long_d128_sampled_rows(nseg):
     _check(inp, nseg, "d128 N=4200", rows=rows)
 
 
+@pytest.mark.parametrize("N", [4096, 4097])
+def test_segmented_at_the_one_work_group_limit(N):
+    # 64 key tiles run in one work-group, 65 in two launches; both at nseg = 3
+    inp = workloads.make_custom(1, N, 2, 2, 128, 96, seed=77)
+    rows = np.array([(0, h, i) for h in range(2) for i in (0, 1365, 1366, 2730, 2731, N - 1)], np.int32)
+    _check(inp, 3, f"d128 N={N}", rows=rows)
+
+
 @pytest.mark.parametrize("N,nseg", [(1, 1), (33, 1), (65, 2), (129, 3), (300, 5), (700, 8)])
 def test_segmented_small_and_ragged_lengths(N, nseg):
     inp = workloads.make_inputs(workloads.CONFIGS["tiny"], N=N)

@@ -43,7 +43,24 @@ __device__ __forceinline__ uint4 load_row8(const View &v, int b, int n, int h, i
     const int nn = valid ? n : 0;
     const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
     const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-    return valid ? make_uint4(x[0], x[1], x[2], x[3]) : make_uint4(0, 0, 0, 0);
+    // the zeroing is an AND with a mask the compiler cannot see through, so
+    // that it does not put the load in a branch on `valid` (a load issued in
+    // a branch makes every later wait for it a wait for all loads)
+    uint32_t m = valid ? 0xffffffffu : 0u;
+    asm("" : "+v"(m));
+    return make_uint4(x[0] & m, x[1] & m, x[2] & m, x[3] & m);
+}
+
+// The same load without the zeroing, for the passes that mask rows >= N
+// themselves (the quantization of Q and K: such rows take no part in the
+// scale and are stored as zeros): no select depends on the loaded value, so
+// the compiler keeps the load where it is written instead of moving it into
+// a branch on the row's validity.
+__device__ __forceinline__ uint4 load_row8_raw(const View &v, int b, int n, int h, int j, bool valid) {
+    const int nn = valid ? n : 0;
+    const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
+    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
 __device__ __forceinline__ void unpack8(uint4 r, float x[8]) {
@@ -58,34 +75,46 @@ __device__ __forceinline__ uint4 pack8(const float y[8]) {
                       pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
 }
 
-// RMSNorm weights of elements [8j, 8j+8) as FP32 (ones when w is NULL),
-// loaded once per kernel.
-__device__ __forceinline__ void load_w8(const uint16_t *w, int j, float wv[8]) {
-    if (w) {
-        unpack8(*reinterpret_cast<const uint4 *>(w + 8 * j), wv);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wv[i] = 1.0f;
-    }
+// Row 0, elements [8j, 8j+8), of head h of batch b: a readable 16-byte
+// aligned address for loads whose value is not used.
+__device__ __forceinline__ const uint16_t *row0_8(const View &v, int b, int h, int j) {
+    return v.ptr + (int64_t)b * v.sb + (int64_t)h * v.sh + 8 * j;
+}
+
+// RMSNorm weights of elements [8j, 8j+8), as their BF16 pairs (BF16 ones,
+// 0x3F80, when w is NULL), loaded once per kernel; unpack8 makes them FP32.
+// Kept packed until first use, so that issuing the load does not wait for it;
+// the load is issued in either case (from `any`, a readable address, when w
+// is NULL) and the ones are merged in with a mask the compiler cannot see
+// through, which keeps the load out of a branch.
+__device__ __forceinline__ uint4 load_w8(const uint16_t *w, int j, const uint16_t *any) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(w ? w + 8 * j : any);
+    uint32_t m = w ? 0xffffffffu : 0u;
+    asm("" : "+v"(m));
+    const uint32_t one = 0x3F803F80u & ~m;
+    return make_uint4((x.x & m) | one, (x.y & m) | one, (x.z & m) | one, (x.w & m) | one);
 }
 
 // RoPE coefficients for elements [8j, 8j+8) at position n when R/2 is a
 // multiple of 8, so that 8-element blocks pair up whole: 16 bytes of cos and
 // of sin at the pair's lower block (lanes past R read block 0 and do not use
-// it).  Unconditional loads, so they can be issued with the row loads.
+// it).
 struct Coef8 {
     uint4 c, s;
 };
 
-__device__ __forceinline__ Coef8 rope_coef8(const uint16_t *cos_t, const uint16_t *sin_t, int n, int j, int R) {
-    Coef8 k = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+// The two loads are issued whatever R is, from `any` (a readable 16-byte
+// aligned address) when the block form does not apply: a load in a branch
+// would make the compiler's later waits count conservatively.  The values are
+// then meaningless, and rope8 does not read them.
+__device__ __forceinline__ Coef8 rope_coef8(const uint16_t *cos_t, const uint16_t *sin_t, int n, int j, int R,
+                                            const uint16_t *any) {
     const int half = R >> 1, d0 = 8 * j;
-    if (R > 0 && (half & 7) == 0) {
-        const int cd = d0 < half ? d0 : (d0 < R ? d0 - half : 0);
-        k.c = *reinterpret_cast<const uint4 *>(cos_t + (int64_t)n * half + cd);
-        k.s = *reinterpret_cast<const uint4 *>(sin_t + (int64_t)n * half + cd);
-    }
-    return k;
+    const bool use = R > 0 && (half & 7) == 0;
+    const int64_t off = (int64_t)n * half + (d0 < half ? d0 : (d0 < R ? d0 - half : 0));
+    const uint16_t *pc = use ? cos_t + off : any;
+    const uint16_t *ps = use ? sin_t + off : any;
+    return Coef8{*reinterpret_cast<const uint4 *>(pc), *reinterpret_cast<const uint4 *>(ps)};
 }
 
 // RMSNorm of one row held by L consecutive lanes (8 elements each).  Every
@@ -215,19 +244,34 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
-    // every global load of the work-group first: K and V rows, RoPE
-    // coefficients, RMSNorm weights
+    // every global load of the work-group first, none of them in a branch
+    // (that would make the compiler's waits count conservatively), in the
+    // order of first use: RMSNorm weights, RoPE coefficients, K rows, V rows
+    // (vmcnt counts in order: waiting for a K row never waits for V)
+    const uint16_t *any = row0_8(p.k, b, h, j);
+    const uint4 wraw = load_w8(p.w_k, j, any);
     uint4 kraw[NPASS], vraw[NPASS];
     Coef8 cf[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int n = t * 64 + pass * RPP + rr;
-        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
-        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
-        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
+        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R, any);
     }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int n = t * 64 + pass * RPP + rr;
+        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int n = t * 64 + pass * RPP + rr;
+        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
+    }
+    // (the compiler's scheduler would otherwise interleave the first passes'
+    // arithmetic with the loads, and their waits with the issue of the rest)
+    __builtin_amdgcn_sched_barrier(0);
     float wv[8];
-    load_w8(p.w_k, j, wv);
+    unpack8(wraw, wv);
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr;
@@ -425,16 +469,29 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
     // next to a store that may alias it, would cost a round trip per pass)
     constexpr bool PRE = NP <= 8;
     constexpr int CG = PRE ? NP : 4;
+    // (the RMSNorm weights and the coefficients before the rows, in the
+    // order of first use, none in a branch)
+    const uint16_t *any = row0_8(p.q, b, h, j);
+    const uint4 wraw = load_w8(p.w_q, j, any);
     uint4 qraw[NP];
     Coef8 cf[CG];
+    if constexpr (PRE) {
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            const int n = 32 * g + pass * RPW + rr;
+            cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R, any);
+        }
+    }
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int n = 32 * g + pass * RPW + rr;
-        qraw[pass] = load_row8(p.q, b, n, h, j, n < p.N);
-        if constexpr (PRE) cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
+        qraw[pass] = load_row8_raw(p.q, b, n, h, j, n < p.N);   // rows >= N are masked below
     }
+    // (the compiler's scheduler would otherwise interleave the first passes'
+    // arithmetic with the loads, and their waits with the issue of the rest)
+    __builtin_amdgcn_sched_barrier(0);
     float wv[8];
-    load_w8(p.w_q, j, wv);
+    unpack8(wraw, wv);
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int r = pass * RPW + rr;
@@ -454,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 #pragma unroll
                 for (int i = 0; i < CG; ++i) {
                     const int ni = 32 * g + (pass + i) * RPW + rr;
-                    cf[i] = rope_coef8(p.cos_t, p.sin_t, ni < p.N ? ni : 0, j, p.R);
+                    cf[i] = rope_coef8(p.cos_t, p.sin_t, ni < p.N ? ni : 0, j, p.R, any);
                 }
             }
         }
@@ -503,22 +560,32 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
-    // every global load of the work-group first: K rows, RoPE coefficients,
-    // RMSNorm weights and the K mean
+    // every global load of the work-group first, none of them in a branch,
+    // in the order of first use: RMSNorm weights, RoPE coefficients, K rows,
+    // the K mean
+    const uint16_t *any = row0_8(p.k, b, h, j);
+    const uint4 wraw = load_w8(p.w_k, j, any);
     uint4 kraw[NPASS];
     Coef8 cf[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int n = t * 64 + pass * RPP + rr;
-        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
-        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R);
+        cf[pass] = rope_coef8(p.cos_t, p.sin_t, n < p.N ? n : 0, j, p.R, any);
     }
-    float wv[8];
-    load_w8(p.w_k, j, wv);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int n = t * 64 + pass * RPP + rr;
+        kraw[pass] = load_row8_raw(p.k, b, n, h, j, n < p.N);   // rows >= N are masked below
+    }
     const float *mu = p.k_mean + ((int64_t)b * p.Hkv + h) * D + 8 * j;
     float mean[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) mean[i] = mu[i];
+    // (the compiler's scheduler would otherwise interleave the first passes'
+    // arithmetic with the loads, and their waits with the issue of the rest)
+    __builtin_amdgcn_sched_barrier(0);
+    float wv[8];
+    unpack8(wraw, wv);
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int r = pass * RPP + rr;

@@ -126,6 +126,24 @@ def test_rope_dims(R):
     _full_check(inp, f"rope_dim={R}")
 
 
+@pytest.mark.parametrize("R,D", [(0, 128), (64, 128), (0, 256), (128, 256)])
+def test_absent_weights_and_tables(R, D):
+    # NULL RMSNorm weights stand for unit weights, and with no rotation the
+    # RoPE tables may be absent as well: the outputs equal those of the unit
+    # weights the inputs are drawn with
+    inp = workloads.make_custom(1, 200, 2, 1, D, R, seed=700 + R + D)
+    banner(f"absent weights, rope_dim={R} D={D}")
+    ref = oracle.prepare(inp)
+    dev = to_device(inp)
+    assert bool((inp.w_q.float() == 1).all()) and bool((inp.w_k.float() == 1).all())
+    dev["w_q"] = dev["w_k"] = None
+    if R == 0:
+        dev["cos"] = dev["sin"] = None
+    shape, bufs, o = run_path(inp, dev=dev)
+    assert_prep_bit_exact(ref, host_tensors(shape, bufs), "absent weights")
+    compare_output(oracle.bf16_to_f32(bf16_bits(o)), oracle.bf16_to_f32(oracle.attention(ref)), "absent weights")
+
+
 def test_extreme_outliers_and_weights():
     inp = workloads.make_custom(1, 333, 3, 3, 128, 96, seed=400, weights=(0.5, 1.5),
                                 outlier_frac=0.02, outlier_mult=1000.0)

@@ -34,33 +34,27 @@ namespace {
 constexpr int kThreads = 256;
 
 // Loads 8 consecutive BF16 values (16 bytes) of row (b, n, h) starting at
-// element 8*j; zeros when the row is invalid.  The load itself is
-// unconditional (an invalid row reads row 0, which always exists), so the
-// kernels can issue every row load of a work-group before using the first.
-// Each pass streams its rows once, far more bytes than the caches hold, so
-// the load is nontemporal.
+// element 8*j.  The load is unconditional (an invalid row reads row 0, which
+// always exists), so the kernels can issue every row load of a work-group
+// before using the first; no select depends on the loaded value, so the
+// compiler keeps the load where it is written instead of moving it into a
+// branch on the row's validity (a load issued in a branch makes every later
+// wait for it a wait for all loads).  Each pass streams its rows once, far
+// more bytes than the caches hold, so the load is nontemporal.
 __device__ __forceinline__ uint4 load_row8(const View &v, int b, int n, int h, int j, bool valid) {
     const int nn = valid ? n : 0;
     const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
     const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-    // the zeroing is an AND with a mask the compiler cannot see through, so
-    // that it does not put the load in a branch on `valid` (a load issued in
-    // a branch makes every later wait for it a wait for all loads)
-    uint32_t m = valid ? 0xffffffffu : 0u;
-    asm("" : "+v"(m));
-    return make_uint4(x[0] & m, x[1] & m, x[2] & m, x[3] & m);
+    return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// The same load without the zeroing, for the passes that mask rows >= N
-// themselves (the quantization of Q and K: such rows take no part in the
-// scale and are stored as zeros): no select depends on the loaded value, so
-// the compiler keeps the load where it is written instead of moving it into
-// a branch on the row's validity.
-__device__ __forceinline__ uint4 load_row8_raw(const View &v, int b, int n, int h, int j, bool valid) {
-    const int nn = valid ? n : 0;
-    const uint16_t *p = v.ptr + (int64_t)b * v.sb + (int64_t)nn * v.sn + (int64_t)h * v.sh + 8 * j;
-    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-    return make_uint4(x[0], x[1], x[2], x[3]);
+// x, or zeros when the row is invalid: an AND with a mask the compiler cannot
+// see through (a select would make it move the row's load into a branch),
+// applied where the row is used, so that it waits for the load there.
+__device__ __forceinline__ uint4 zero_unless(uint4 x, bool valid) {
+    uint32_t m = valid ? 0xffffffffu : 0u;
+    asm("" : "+v"(m));
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
 }
 
 __device__ __forceinline__ void unpack8(uint4 r, float x[8]) {
@@ -260,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int n = t * 64 + pass * RPP + rr;
-        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);
+        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);     // rows >= N are zeroed after RoPE
     }
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
@@ -298,7 +292,8 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const PrepParams p
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         float x[8];
-        unpack8(vraw[pass], x);                            // invalid rows are zeros
+        const int n = t * 64 + pass * RPP + rr;
+        unpack8(zero_unless(vraw[pass], n < p.N), x);     // invalid rows are zeros
 #pragma unroll
         for (int i = 0; i < 8; ++i) vm[i] = __builtin_fmaxf(vm[i], __builtin_fabsf(x[i]));
     }
@@ -485,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         const int n = 32 * g + pass * RPW + rr;
-        qraw[pass] = load_row8_raw(p.q, b, n, h, j, n < p.N);   // rows >= N are masked below
+        qraw[pass] = load_row8(p.q, b, n, h, j, n < p.N);   // rows >= N are masked below
     }
     // (the compiler's scheduler would otherwise interleave the first passes'
     // arithmetic with the loads, and their waits with the issue of the rest)
@@ -546,15 +541,25 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2b: K -> subtract k_mean -> INT8, one scale per 64-row tile.
-// Grid (nk * Hkv, B), x = tile * Hkv + head.
+// Pass 2b: one 64-row tile of K and of V per work-group.  Grid (nk * Hkv, B),
+// x = tile * Hkv + head.
+//   K -> subtract k_mean -> INT8, one scale per tile;
+//   V -> E4M3 into tiles [D][64], keys of a tile in the slot order of
+//        sage_v8_slot_key (the key order in which the attention kernel holds
+//        its probabilities), one scale per channel (from pass 1).
+// The two share a work-group so that the V rows, which need no arithmetic
+// before their conversion, stream in while the K rows are normalized and
+// rotated.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
+__global__ __launch_bounds__(kThreads) void quant_kv_kernel(const PrepParams p) {
     constexpr int L = D / 8;
     constexpr int RPP = kThreads / L;
     constexpr int NPASS = 64 / RPP;
+    constexpr int NE = 2 * D / kThreads;      // V conversion items per thread
+    static_assert(NE * kThreads == 2 * D, "whole conversion items per thread");
     __shared__ __attribute__((aligned(16))) uint16_t ybuf[64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[64 * D];
     __shared__ float wmax[kThreads / 64];
 
     const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
@@ -562,10 +567,11 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
 
     // every global load of the work-group first, none of them in a branch,
     // in the order of first use: RMSNorm weights, RoPE coefficients, K rows,
-    // the K mean
+    // the K mean, V rows, the V channel maxima (vmcnt counts in order:
+    // waiting for a K row never waits for V)
     const uint16_t *any = row0_8(p.k, b, h, j);
     const uint4 wraw = load_w8(p.w_k, j, any);
-    uint4 kraw[NPASS];
+    uint4 kraw[NPASS], vraw[NPASS];
     Coef8 cf[NPASS];
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
@@ -575,12 +581,23 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
         const int n = t * 64 + pass * RPP + rr;
-        kraw[pass] = load_row8_raw(p.k, b, n, h, j, n < p.N);   // rows >= N are masked below
+        kraw[pass] = load_row8(p.k, b, n, h, j, n < p.N);   // rows >= N are masked below
     }
     const float *mu = p.k_mean + ((int64_t)b * p.Hkv + h) * D + 8 * j;
     float mean[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) mean[i] = mu[i];
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int n = t * 64 + pass * RPP + rr;
+        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
+    }
+    // thread: channel pair (2 dp, 2 dp + 1) and a quarter qr of the 64 slots
+    // for each of its NE items e = tid + kThreads * i
+    const float *vam = p.ws_vamax + ((int64_t)b * p.Hkv + h) * D;
+    float2 am[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) am[i] = *reinterpret_cast<const float2 *>(vam + 2 * ((tid + kThreads * i) % (D / 2)));
     // (the compiler's scheduler would otherwise interleave the first passes'
     // arithmetic with the loads, and their waits with the issue of the rest)
     __builtin_amdgcn_sched_barrier(0);
@@ -593,7 +610,17 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
         unpack8(kraw[pass], x);
         *reinterpret_cast<uint4 *>(&ybuf[r * D + 8 * j]) = rmsnorm8<L>(x, wv, p.eps, D);
     }
+    // (the V rows go to LDS after the K passes: stored first, their waits
+    // would be every load's)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int n = t * 64 + pass * RPP + rr;
+        *reinterpret_cast<uint4 *>(&vbuf[(pass * RPP + rr) * D + 8 * j]) = zero_unless(vraw[pass], n < p.N);
+    }
     __syncthreads();
+
+    // K
     float u[NPASS][8];
     float amax = 0.0f;
 #pragma unroll
@@ -632,56 +659,31 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const PrepParams p) {
         *reinterpret_cast<uint2 *>(dst + (int64_t)r * D + 8 * j) = make_uint2(lo, hi);
     }
     if (tid == 0) p.k_scale[((int64_t)b * p.Hkv + h) * p.nk + t] = scale;
-}
 
-// ---------------------------------------------------------------------------
-// Pass 2c: V -> E4M3 into tiles [D][64], keys of a tile in the slot order of
-// sage_v8_slot_key (the key order in which the attention kernel holds its
-// probabilities).  Grid (nk * Hkv, B), x = tile * Hkv + head.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) void quant_v_kernel(const PrepParams p) {
-    constexpr int L = D / 8;
-    constexpr int RPP = kThreads / L;
-    constexpr int NPASS = 64 / RPP;
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[64 * D];
-
-    const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
-    const int tid = threadIdx.x, j = tid % L, rr = tid / L;
-    uint4 vraw[NPASS];
+    // V: for each slot, one 4-byte LDS read gives both channels of its key
+    uint8_t *vdst = p.v8 + (((int64_t)b * p.Hkv + h) * p.nk + t) * (int64_t)D * 64;
 #pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
-        const int n = t * 64 + pass * RPP + rr;
-        vraw[pass] = load_row8(p.v, b, n, h, j, n < p.N);
-    }
-#pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass)
-        *reinterpret_cast<uint4 *>(&vbuf[(pass * RPP + rr) * D + 8 * j]) = vraw[pass];
-    __syncthreads();
-    // thread: channel pair (2 dp, 2 dp + 1) and a quarter qr of the 64 slots;
-    // for each slot, one 4-byte LDS read gives both channels of its key
-    const float *amax = p.ws_vamax + ((int64_t)b * p.Hkv + h) * D;
-    uint8_t *dst = p.v8 + (((int64_t)b * p.Hkv + h) * p.nk + t) * (int64_t)D * 64;
-    for (int e = tid; e < 2 * D; e += kThreads) {
+    for (int i = 0; i < NE; ++i) {
+        const int e = tid + kThreads * i;
         const int dp = e % (D / 2), qr = e / (D / 2);
         const int d = 2 * dp;
-        const float mul0 = 2.25f / amax[d], mul1 = 2.25f / amax[d + 1];
+        const float mul0 = 2.25f / am[i].x, mul1 = 2.25f / am[i].y;
         uint32_t w0[4], w1[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             float x0[4], x1[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = sage_v8_slot_key(16 * qr + 4 * k + i);
+            for (int q = 0; q < 4; ++q) {
+                const int key = sage_v8_slot_key(16 * qr + 4 * k + q);
                 const uint32_t pair = *reinterpret_cast<const uint32_t *>(&vbuf[key * D + d]);
-                x0[i] = bf16_lo(pair) * mul0;
-                x1[i] = bf16_hi(pair) * mul1;
+                x0[q] = bf16_lo(pair) * mul0;
+                x1[q] = bf16_hi(pair) * mul1;
             }
             w0[k] = pack4_e4m3_bounded(x0);
             w1[k] = pack4_e4m3_bounded(x1);
         }
-        *reinterpret_cast<uint4 *>(dst + (int64_t)d * 64 + 16 * qr) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-        *reinterpret_cast<uint4 *>(dst + (int64_t)(d + 1) * 64 + 16 * qr) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        *reinterpret_cast<uint4 *>(vdst + (int64_t)d * 64 + 16 * qr) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4 *>(vdst + (int64_t)(d + 1) * 64 + 16 * qr) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
     }
 }
 
@@ -708,12 +710,10 @@ hipError_t sage_launch_quant(const PrepParams &p, hipStream_t s) {
     const dim3 gk((unsigned)(p.nk * p.Hkv), p.B);
     if (p.D == 128) {
         sage::quant_q_kernel<128><<<gq, sage::kThreads, 0, s>>>(p);
-        sage::quant_k_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
-        sage::quant_v_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
+        sage::quant_kv_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
     } else {
         sage::quant_q_kernel<256><<<gq, sage::kThreads, 0, s>>>(p);
-        sage::quant_k_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
-        sage::quant_v_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
+        sage::quant_kv_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
     }
     return hipGetLastError();
 }

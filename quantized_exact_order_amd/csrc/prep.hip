@@ -441,31 +441,35 @@ __global__ __launch_bounds__(kRedCols * kRedMaxGroups) void prep_reduce_kernel(c
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2a: Q -> INT8, one scale per 32 rows.  Grid (q_rows/128 * Hq, B),
-// x = (row block) * Hq + head; wave w of row block r owns group g = 4r + w
-// (rows [32g, 32g+32)).
+// Pass 2a: Q -> INT8, one scale per 32 rows.  Work-group x of batch b
+// (x < q_rows/128 * Hq): x = (row block) * Hq + head; wave w of row block r
+// owns group g = 4r + w (rows [32g, 32g+32)).  LDS: kQLds(D) bytes.
 // ---------------------------------------------------------------------------
+constexpr int kQLds(int D) { return 4 * 32 * D * 2; }
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
+__device__ __forceinline__ void quant_q_tile(const PrepParams &p, int x, int b, uint8_t *lds) {
     constexpr int L = D / 8;
     constexpr int RPW = 64 / L;            // rows per wave pass
     constexpr int NP = 32 / RPW;
-    __shared__ __attribute__((aligned(16))) uint16_t ybuf[4][32 * D];
 
-    const int h = blockIdx.x % p.Hq, b = blockIdx.y;
+    const int h = x % p.Hq;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane % L, rr = lane / L;
-    const int g = (blockIdx.x / p.Hq) * 4 + wave;
-    uint16_t *yb = ybuf[wave];
+    const int g = (x / p.Hq) * 4 + wave;
+    uint16_t *yb = reinterpret_cast<uint16_t *>(lds) + wave * 32 * D;
 
-    // every row load of the wave first, then the RoPE coefficients: all of
-    // them when they fit in registers, else in groups of CG passes, each
+    // every row load of the wave first; the RoPE coefficients with them when
+    // there are at most 4 passes, else in groups of CG = 4 passes, each
     // group's loads issued together ahead of its passes (a load per pass,
-    // next to a store that may alias it, would cost a round trip per pass)
-    constexpr bool PRE = NP <= 8;
+    // next to a store that may alias it, would cost a round trip per pass).
+    // Loading all 8 groups of D = 128 up front takes 136 VGPRs, which leaves
+    // the launch shared with the K/V work-groups at 3 work-groups per CU
+    // instead of 4, and measured 5% slower.
+    constexpr bool PRE = NP <= 4;
     constexpr int CG = PRE ? NP : 4;
-    // (the RMSNorm weights and the coefficients before the rows, in the
-    // order of first use, none in a branch)
+    // (the RMSNorm weights, and the coefficients when loaded up front, before
+    // the rows, in the order of first use, none in a branch)
     const uint16_t *any = row0_8(p.q, b, h, j);
     const uint4 wraw = load_w8(p.w_q, j, any);
     uint4 qraw[NP];
@@ -541,8 +545,8 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2b: one 64-row tile of K and of V per work-group.  Grid (nk * Hkv, B),
-// x = tile * Hkv + head.
+// Pass 2b: one 64-row tile of K and of V per work-group.  Work-group x of
+// batch b (x < nk * Hkv): x = tile * Hkv + head.  LDS: kKVLds(D) bytes.
 //   K -> subtract k_mean -> INT8, one scale per tile;
 //   V -> E4M3 into tiles [D][64], keys of a tile in the slot order of
 //        sage_v8_slot_key (the key order in which the attention kernel holds
@@ -551,18 +555,20 @@ __global__ __launch_bounds__(kThreads) void quant_q_kernel(const PrepParams p) {
 // before their conversion, stream in while the K rows are normalized and
 // rotated.
 // ---------------------------------------------------------------------------
+constexpr int kKVLds(int D) { return 2 * 64 * D * 2 + 16 * (kThreads / 64); }
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void quant_kv_kernel(const PrepParams p) {
+__device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int x, int b, uint8_t *lds) {
     constexpr int L = D / 8;
     constexpr int RPP = kThreads / L;
     constexpr int NPASS = 64 / RPP;
     constexpr int NE = 2 * D / kThreads;      // V conversion items per thread
     static_assert(NE * kThreads == 2 * D, "whole conversion items per thread");
-    __shared__ __attribute__((aligned(16))) uint16_t ybuf[64 * D];
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[64 * D];
-    __shared__ float wmax[kThreads / 64];
+    uint16_t *ybuf = reinterpret_cast<uint16_t *>(lds);
+    uint16_t *vbuf = ybuf + 64 * D;
+    float *wmax = reinterpret_cast<float *>(vbuf + 64 * D);
 
-    const int h = blockIdx.x % p.Hkv, t = blockIdx.x / p.Hkv, b = blockIdx.y;
+    const int h = x % p.Hkv, t = x / p.Hkv;
     const int tid = threadIdx.x, j = tid % L, rr = tid / L;
 
     // every global load of the work-group first, none of them in a branch,
@@ -687,6 +693,30 @@ __global__ __launch_bounds__(kThreads) void quant_kv_kernel(const PrepParams p) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pass 2 as one launch.  Grid (nq_wg + nkv_wg, B) with nq_wg = q_rows/128 * Hq
+// Q work-groups and nkv_wg = nk * Hkv K/V work-groups, interleaved in runs of
+// one Q and two K/V work-groups while both last (then the rest of either
+// kind), so that the Q passes' arithmetic and the K/V streams share the CUs
+// throughout the launch.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_kernel(const PrepParams p, int nq_wg, int nkv_wg) {
+    constexpr int kLds = kQLds(D) > kKVLds(D) ? kQLds(D) : kKVLds(D);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+    const int i = blockIdx.x, b = blockIdx.y;
+    const int u = min(nq_wg, nkv_wg / 2);     // runs of (Q, K/V, K/V)
+    if (i < 3 * u) {
+        const int run = i / 3, r = i - 3 * run;
+        if (r == 0) quant_q_tile<D>(p, run, b, lds);
+        else quant_kv_tile<D>(p, 2 * run + r - 1, b, lds);
+    } else if (i < 3 * u + (nq_wg - u)) {
+        quant_q_tile<D>(p, u + (i - 3 * u), b, lds);
+    } else {
+        quant_kv_tile<D>(p, 2 * u + (i - 3 * u - (nq_wg - u)), b, lds);
+    }
+}
+
 }  // namespace
 }  // namespace sage
 
@@ -706,14 +736,9 @@ hipError_t sage_launch_prep_stats(const PrepParams &p, hipStream_t s) {
 }
 
 hipError_t sage_launch_quant(const PrepParams &p, hipStream_t s) {
-    const dim3 gq((unsigned)(p.q_rows / 128 * p.Hq), p.B);
-    const dim3 gk((unsigned)(p.nk * p.Hkv), p.B);
-    if (p.D == 128) {
-        sage::quant_q_kernel<128><<<gq, sage::kThreads, 0, s>>>(p);
-        sage::quant_kv_kernel<128><<<gk, sage::kThreads, 0, s>>>(p);
-    } else {
-        sage::quant_q_kernel<256><<<gq, sage::kThreads, 0, s>>>(p);
-        sage::quant_kv_kernel<256><<<gk, sage::kThreads, 0, s>>>(p);
-    }
+    const int nq_wg = (int)(p.q_rows / 128 * p.Hq), nkv_wg = p.nk * p.Hkv;
+    const dim3 grid((unsigned)(nq_wg + nkv_wg), p.B);
+    if (p.D == 128) sage::quant_kernel<128><<<grid, sage::kThreads, 0, s>>>(p, nq_wg, nkv_wg);
+    else sage::quant_kernel<256><<<grid, sage::kThreads, 0, s>>>(p, nq_wg, nkv_wg);
     return hipGetLastError();
 }

@@ -1037,8 +1037,9 @@ __global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnPa
     wait_vm0();
 
     const float dt = dsum + shfl_xor_f(dsum, 32);
-    if (seg > 0) {
-        // the segment's RO into its own region as [blk][r4][lane] float4
+    // every segment's RO into its own region as [blk][r4][lane] float4, and
+    // its (m, d) per row
+    {
         float4 *ro_w = reinterpret_cast<float4 *>(region);
 #pragma unroll
         for (int blk = 0; blk < KS; ++blk)
@@ -1048,48 +1049,88 @@ __global__ __launch_bounds__(64 * kSegWgMax) void attn_segwg_kernel(const AttnPa
                     make_float4(acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
         if (hi == 0) md_s[seg][col] = make_float2(m, dt);
     }
-    // wave 0: the output's V scales go out before the wait for the others
-    float4 sc[4][4];
-    if (seg == 0) load_o_scales(p.v_scale + ((int64_t)b * p.Hkv + hk) * D, lane, sc);
-    __syncthreads();
-    if (seg > 0) return;
-    // combine in increasing segment order: M = max m_s, a_s = exp2(m_s - M),
-    // d = sum d_s a_s, RO = sum RO_s a_s (from 0)
-    float2 mds[kSegWgMax];
-#pragma unroll
-    for (int s = 1; s < kSegWgMax; ++s)
-        if (s < nseg) mds[s] = md_s[s][col];
-    float M = __builtin_fmaxf(-INFINITY, m);
-#pragma unroll
-    for (int s = 1; s < kSegWgMax; ++s)
-        if (s < nseg) M = __builtin_fmaxf(M, mds[s].x);
-    const float a0 = __builtin_amdgcn_exp2f(m - M);
-    float d = 0.0f + dt * a0;
+    // wave w combines the 32-channel blocks w, w + nseg, ... of all segments;
+    // their V scales go out before the barrier
+    const float *vs = p.v_scale + ((int64_t)b * p.Hkv + hk) * D;
+    float4 sc[KS][4];
 #pragma unroll
     for (int blk = 0; blk < KS; ++blk)
+        if (blk % nseg == seg)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[blk][i] = 0.0f + acc[blk][i] * a0;
+            for (int r4 = 0; r4 < 4; ++r4) sc[blk][r4] = *reinterpret_cast<const float4 *>(vs + 32 * blk + 8 * r4 + 4 * hi);
+    __syncthreads();
+    if (seg < KS) {
+        // in increasing segment order: M = max m_s, a_s = exp2(m_s - M),
+        // d = sum d_s a_s, RO = sum RO_s a_s (from 0), then O as in the
+        // exact epilogue; every combining wave forms the same d
+        float2 mds[kSegWgMax];
 #pragma unroll
-    for (int s = 1; s < kSegWgMax; ++s) {
-        if (s >= nseg) break;
-        const float a = __builtin_amdgcn_exp2f(mds[s].x - M);
-        d = d + mds[s].y * a;
-        const float4 *ro_r = reinterpret_cast<const float4 *>(segwg_lds + s * kSegWgRegion);
+        for (int s = 0; s < kSegWgMax; ++s)
+            if (s < nseg) mds[s] = md_s[s][col];
+        float M = __builtin_fmaxf(-INFINITY, mds[0].x);
 #pragma unroll
-        for (int blk = 0; blk < KS; ++blk)
+        for (int s = 1; s < kSegWgMax; ++s)
+            if (s < nseg) M = __builtin_fmaxf(M, mds[s].x);
+        float a[kSegWgMax];
+        float d = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kSegWgMax; ++s)
+            if (s < nseg) {
+                a[s] = __builtin_amdgcn_exp2f(mds[s].x - M);
+                d = d + mds[s].y * a[s];
+            }
+        const float rinv = 1.0f / d;
+#pragma unroll
+        for (int blk = 0; blk < KS; ++blk) {
+            if (blk % nseg != seg) continue;
+            float r[16];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 v = ro_r[(blk * 4 + r4) * 64 + lane];
-                acc[blk][4 * r4 + 0] = acc[blk][4 * r4 + 0] + v.x * a;
-                acc[blk][4 * r4 + 1] = acc[blk][4 * r4 + 1] + v.y * a;
-                acc[blk][4 * r4 + 2] = acc[blk][4 * r4 + 2] + v.z * a;
-                acc[blk][4 * r4 + 3] = acc[blk][4 * r4 + 3] + v.w * a;
+                const float4 v = reinterpret_cast<const float4 *>(segwg_lds)[(blk * 4 + r4) * 64 + lane];
+                r[4 * r4 + 0] = 0.0f + v.x * a[0];
+                r[4 * r4 + 1] = 0.0f + v.y * a[0];
+                r[4 * r4 + 2] = 0.0f + v.z * a[0];
+                r[4 * r4 + 3] = 0.0f + v.w * a[0];
             }
+#pragma unroll
+            for (int s = 1; s < kSegWgMax; ++s) {
+                if (s >= nseg) break;
+                const float4 *ro_r = reinterpret_cast<const float4 *>(segwg_lds + s * kSegWgRegion);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 v = ro_r[(blk * 4 + r4) * 64 + lane];
+                    r[4 * r4 + 0] = r[4 * r4 + 0] + v.x * a[s];
+                    r[4 * r4 + 1] = r[4 * r4 + 1] + v.y * a[s];
+                    r[4 * r4 + 2] = r[4 * r4 + 2] + v.z * a[s];
+                    r[4 * r4 + 3] = r[4 * r4 + 3] + v.w * a[s];
+                }
+            }
+            // the block's BF16 output, 32 rows x 64 bytes, into region 0's
+            // slice of this block (read above by this wave only), 16-byte
+            // chunks XOR-swizzled by row
+            uint8_t *st = segwg_lds + blk * 4096;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float o_0 = (r[4 * r4 + 0] * rinv) * sc[blk][r4].x;
+                const float o_1 = (r[4 * r4 + 1] * rinv) * sc[blk][r4].y;
+                const float o_2 = (r[4 * r4 + 2] * rinv) * sc[blk][r4].z;
+                const float o_3 = (r[4 * r4 + 3] * rinv) * sc[blk][r4].w;
+                *reinterpret_cast<uint2 *>(st + col * 64 + 16 * (r4 ^ ((col >> 2) & 3)) + 8 * hi) =
+                    make_uint2(pack_bf16x2(o_0, o_1), pack_bf16x2(o_2, o_3));
+            }
+        }
     }
-    const float rinv = 1.0f / d;
-    // wave 0's own region (its tiles are done) is the output stage
-    store_o_block(p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh, p.osn, p.N - q0, segwg_lds,
-                  sc, lane, acc, rinv);
+    __syncthreads();
+    // every wave stores: row r's 16-byte chunk c holds channels 8c .. 8c + 7,
+    // staged by the wave of block c / 4; 16 lanes write a row's 256 bytes
+    uint16_t *o0 = p.o + (int64_t)b * p.osb + (int64_t)q0 * p.osn + (int64_t)h * p.osh;
+    const int nvalid = p.N - q0;
+    for (int idx = tid; idx < 32 * 16; idx += 64 * nseg) {
+        const int r = idx >> 4, c = idx & 15;
+        const uint4 v =
+            *reinterpret_cast<const uint4 *>(segwg_lds + (c >> 2) * 4096 + r * 64 + 16 * ((c & 3) ^ ((r >> 2) & 3)));
+        if (r < nvalid) *reinterpret_cast<uint4 *>(o0 + (int64_t)r * p.osn + 8 * c) = v;
+    }
     stamp_store(p.stamps, st0);
 }
 

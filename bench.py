@@ -664,7 +664,7 @@ def run_prefill(args, name):
             "clock_note": clock["note"],
         },
         "prep": {
-            "kernels": "sage_prep + sage_quant_qk (6 launches)",
+            "kernels": "sage_prep + sage_quant_qk (3 launches: prep_stats, prep_reduce, quant)",
             "avg_ms": round(prep_avg_ms, 4),
             "algorithmic_bytes": int(prep_bytes),
             "GB_per_s": round(prep_bytes / (prep_avg_ms * 1e-3) / 1e9, 1),

@@ -11,17 +11,20 @@
 //     division and square root, y = bf16((x*inv)*w);
 //   * RoPE: z_i = bf16(a*c - b*s), z_{i+R/2} = bf16(b*c + a*s) on BF16 y and
 //     BF16 coefficients (products exact in FP32);
-//   * K mean: pairwise tree over the sequence padded with +0 to a power of two
-//     (>= 64): an in-tile tree over 64 rows here, a tree over tiles in
-//     prep_reduce_kernel;
+//   * K mean: pairwise tree over the sequence padded with +0 to
+//     2^ceil(log2 N) leaves: an in-tile tree over 64 rows here (cut short for
+//     a sequence of one tile), a tree over tiles in prep_reduce_kernel;
 //   * quantization: amax = max(1e-7, max|u|), scale = amax/127,
 //     q = rni_sat(u * (127/amax)); V: v_scale = amax/2.25,
 //     v8 = e4m3_rn_satfinite(v * (2.25/amax)).
 // The file is built with -ffp-contract=off: no multiply-add is fused.
 //
-// HBM-bound: each kernel streams its rows once with 16-byte loads (one row
-// of D BF16 values is D/8 lanes), keeps per-row work in registers and uses LDS
-// only for the RoPE partner exchange and the 64-row column reductions.
+// Two passes over the rows: prep_stats_kernel (K tile sums, V tile maxima)
+// and prep_reduce_kernel, then quant_kernel, one launch for the quantization
+// of Q, K and V.  Each kernel streams its rows once with 16-byte loads (one
+// row of D BF16 values is D/8 lanes), keeps per-row work in registers and
+// uses LDS only for the RoPE partner exchange, the 64-row column reductions
+// and the V tile transpose.
 
 #include <algorithm>
 

@@ -58,8 +58,10 @@ typedef enum sage_status {
 /* Problem shape.
  *   B, N      batch and sequence length (1 <= N <= 2^24)
  *   Hq, Hkv   query and key/value heads; query head h reads KV head h/(Hq/Hkv);
- *             B * Hq * ceil(N/64) must stay below 2^31 (work-groups of one
- *             launch), else SAGE_E_SHAPE
+ *             every launch must fit one dispatch of at most 2^32 - 1
+ *             work-items along its grid's x dimension, else SAGE_E_SHAPE:
+ *             ceil(N/128) * Hq * B * 256 (512 for D = 256) and
+ *             (ceil(N/128) * Hq + ceil(N/64) * Hkv) * 256
  *   D         head dimension, 128 or 256
  *   rope_dim  R: split-half RoPE rotates dims [0, R) in pairs (i, i + R/2);
  *             even, 0 <= R <= D (96 for D = 128 on the contract page)
@@ -193,7 +195,8 @@ sage_status sage_wall_clock_khz(int32_t *khz);
  *   workspace  device memory of at least sage_attn_segmented_workspace bytes,
  *              16-byte aligned: the runs' FP32 partials (RO, m, d)
  * Refusals: those of sage_attn_fwd, SAGE_E_SHAPE (nseg out of range, or
- * B * Hq * nseg * ceil(N/128) >= 2^31 work-groups), SAGE_E_WORKSPACE,
+ * ceil(N/128) * nseg * Hq * B * 256 (512 for D = 256) >= 2^32 work-items),
+ * SAGE_E_WORKSPACE,
  * SAGE_E_ALIGN (workspace). */
 sage_status sage_attn_segmented_workspace(const sage_shape *shape, int32_t nseg, size_t *bytes);
 sage_status sage_attn_fwd_segmented(const sage_shape *shape, const sage_bufs *bufs, int32_t nseg, void *o,
@@ -241,8 +244,9 @@ typedef struct sage_kv_cache {
  * values).
  * Refusals: SAGE_E_NULL (also: both or neither of v and v8 set, or v8
  * without v_scale), SAGE_E_UNSUPPORTED (D != 256), SAGE_E_SHAPE
- * (B, Hkv, capacity not a multiple of 8, n < 1, t0 < 0 or
- * t0 + n > capacity), SAGE_E_STRIDE,
+ * (B, Hkv, capacity not a multiple of 8, n < 1, t0 < 0,
+ * t0 + n > capacity, or more than 2^26 - 1 blocks of 8 tokens times Hkv,
+ * the work-items one dispatch holds), SAGE_E_STRIDE,
  * SAGE_E_ALIGN, SAGE_E_HIP. */
 sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, const sage_view_bf16 *v,
                            int32_t t0, int32_t n, void *stream);

@@ -15,6 +15,8 @@ hipError_t sage_launch_primitive(int kind, uint32_t first, uint32_t count, void 
 namespace {
 
 constexpr int64_t kMaxN = int64_t(1) << 24;
+// A dispatch holds its grid size in work-items as 32 bits per dimension.
+constexpr int64_t kMaxItems = 4294967295LL;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -25,8 +27,14 @@ sage_status check_shape(const sage_shape *s) {
     if (s->B < 1 || s->N < 1 || s->N > kMaxN || s->Hq < 1 || s->Hkv < 1) return SAGE_E_SHAPE;
     if (s->D != 128 && s->D != 256) return SAGE_E_SHAPE;
     if ((int64_t)s->B * s->Hq > 65535 * 64 || s->B > 65535 || s->Hq > 65535) return SAGE_E_SHAPE;
-    // every launch covers at most B * Hq * ceil(N/64) work-groups in one dimension
-    if ((int64_t)s->B * s->Hq * ((s->N + 63) / 64) > 2147483647) return SAGE_E_SHAPE;
+    // every launch fits one dispatch: the attention grid (ceil(N/128) * Hq * B
+    // work-groups of 256 threads, 512 for D = 256) and the quantization grid
+    // (ceil(N/128) * Hq + ceil(N/64) * Hkv work-groups of 256 threads per
+    // batch row) hold at most kMaxItems work-items; the other preparation
+    // grids are smaller
+    const int64_t nqt = (s->N + 127) / 128, nkt = (s->N + 63) / 64;
+    if (nqt * s->Hq * s->B * (s->D == 256 ? 512 : 256) > kMaxItems) return SAGE_E_SHAPE;
+    if ((nqt * s->Hq + nkt * s->Hkv) * 256 > kMaxItems) return SAGE_E_SHAPE;
     if (s->Hq % s->Hkv != 0) return SAGE_E_GQA;
     if (s->rope_dim < 0 || s->rope_dim > s->D || (s->rope_dim & 1)) return SAGE_E_ROPE;
     if (s->hadamard != 0 && s->hadamard != 1) return SAGE_E_UNSUPPORTED;
@@ -188,7 +196,7 @@ sage_status check_nseg(const sage_shape *shape, int32_t nseg) {
     // the two-launch form: 128 query rows per work-group and segment (the
     // one-work-group form checks its own grid and otherwise takes this one)
     const int64_t nqt = (shape->N + 127) / 128;
-    if (nqt * nseg * shape->Hq * shape->B > 2147483647LL) return SAGE_E_SHAPE;
+    if (nqt * nseg * shape->Hq * shape->B * (shape->D == 256 ? 512 : 256) > kMaxItems) return SAGE_E_SHAPE;
     if (seg_ro_bytes(shape, nseg) == 0) return SAGE_E_SHAPE;
     return SAGE_OK;
 }
@@ -286,7 +294,8 @@ sage_status sage_kv_append(const sage_kv_cache *cache, const sage_view_bf16 *k, 
     if ((st = check_view(v)) != SAGE_OK) return st;
     if (n < 1 || t0 < 0 || (int64_t)t0 + n > cache->capacity) return SAGE_E_SHAPE;
     const int64_t nblk = ((int64_t)t0 + n - 1) / sage::kVBlock - t0 / sage::kVBlock + 1;
-    if (nblk * cache->Hkv > 2147483647LL - 3) return SAGE_E_SHAPE;
+    // (nblk * Hkv + 3) / 4 work-groups of 256 threads
+    if ((nblk * cache->Hkv + 3) / 4 * 256 > kMaxItems) return SAGE_E_SHAPE;
     sage::KvAppendParams p;
     std::memset(&p, 0, sizeof(p));
     p.B = cache->B; p.Hkv = cache->Hkv; p.D = cache->D; p.n = n; p.t0 = t0; p.cap = cache->capacity;
@@ -325,7 +334,7 @@ sage_status build_decode(const sage_kv_cache *cache, int32_t Hq, const sage_view
     if (grp > sage::kDecodeMaxGroup) return SAGE_E_UNSUPPORTED;
     if ((st = sage_decode_workspace(cache, Hq, T, need)) != SAGE_OK) return st;
     const int64_t nchunk = sage::decode_nchunk(cache->B, cache->Hkv, T);
-    if (nchunk * cache->Hkv > 2147483647LL) return SAGE_E_SHAPE;
+    if (nchunk * cache->Hkv * 256 > kMaxItems) return SAGE_E_SHAPE;
     std::memset(p, 0, sizeof(*p));
     p->B = cache->B; p->Hq = Hq; p->Hkv = cache->Hkv; p->grp = grp; p->D = cache->D; p->T = T;
     p->cap = cache->capacity;

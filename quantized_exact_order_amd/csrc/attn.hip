@@ -1187,7 +1187,7 @@ hipError_t sage_launch_attn_segmented(const sage::AttnParams &p, int D, hipStrea
     // short sequences with few segments: one launch, segments combined in LDS
     // (the same bytes as the two-launch form below)
     const int64_t nqb32 = (p.N + 31) / 32;
-    if (D == 128 && p.nseg <= sage::kSegWgMax && p.nk <= 64 && nqb32 * p.Hq * p.B <= 2147483647LL) {
+    if (D == 128 && p.nseg <= sage::kSegWgMax && p.nk <= 64 && nqb32 * p.Hq * p.B * 64 * p.nseg <= 4294967295LL) {
         const unsigned nqb = (unsigned)nqb32;
         const size_t lds = (size_t)p.nseg * sage::kSegWgRegion;
         if (lds > 65536) {

@@ -64,8 +64,10 @@ def test_v8_slot_order_is_a_permutation(sage):
     (dict(rope_dim=95), "SAGE_E_ROPE"), (dict(rope_dim=130), "SAGE_E_ROPE"),
     (dict(rope_dim=-2), "SAGE_E_ROPE"), (dict(hadamard=True), "SAGE_E_UNSUPPORTED"),
     (dict(eps=0.0), "SAGE_E_UNSUPPORTED"), (dict(eps=float("nan")), "SAGE_E_UNSUPPORTED"),
-    # 4096 * 64 heads * 16384 key tiles = 2^32 work-groups in one launch
+    # 4096 * 64 heads * 8192 query tiles of 256 threads: 2^39 work-items in one launch
     (dict(B=4096, Hq=64, Hkv=64, N=1 << 20), "SAGE_E_SHAPE"),
+    # the quantization grid, (86 + 171) * 65535 work-groups of 256 threads, past 2^32 - 1
+    (dict(Hq=65535, Hkv=65535, N=64 * 171), "SAGE_E_SHAPE"),
 ])
 def test_shape_refusals(sage, kw, err):
     base = dict(B=1, N=100, Hq=4, Hkv=2, D=128, rope_dim=96, hadamard=False, eps=1e-5)
@@ -144,16 +146,17 @@ def test_segmented_refusals_happen_before_launch(sage):
     assert call(2, wsb=16) == "SAGE_E_WORKSPACE"
     assert call(2, wsp=None) == "SAGE_E_WORKSPACE"
     assert call(2, wsp=A + 8) == "SAGE_E_ALIGN"
-    # the grid limit counts the segments: ceil(N/128) * Hq = 16384 * 65535 work-groups per
-    # segment, so 2 segments (2,147,450,880) fit under 2^31 - 1 and 3 do not
-    big = sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96)
+    # the grid limit counts the segments: ceil(N/128) * Hq * 256 = 131071 * 64 * 256 work-items
+    # per segment, so 2 segments (4,294,934,528) fit under 2^32 - 1 and 3 do not
+    big = sage.Shape(1, 128 * 131071, 64, 1, 128, 96)
     assert ws(2, big) == "SAGE_OK" and ws(3, big) == "SAGE_E_SHAPE"
 
 
 def test_largest_grid_is_accepted(sage):
-    # 2^31 - 1 work-groups is the limit; just under it is accepted
-    z = sage.buffer_sizes(sage.Shape(1, 64 * 32767, 65535, 65535, 128, 96))
-    assert z.n_k_tiles == 32767
+    # 2^32 - 1 work-items per dispatch is the limit; the quantization grid of
+    # (85 + 170) * 65535 work-groups of 256 threads (4,278,190,080) is just under it
+    z = sage.buffer_sizes(sage.Shape(1, 64 * 170, 65535, 65535, 128, 96))
+    assert z.n_k_tiles == 170
 
 
 def test_decode_cache_refusals_happen_before_launch(sage):
@@ -171,6 +174,8 @@ def test_decode_cache_refusals_happen_before_launch(sage):
     assert append(cache(), 0, 0) == "SAGE_E_SHAPE"
     assert append(cache(v=A + 4), 0, 1) == "SAGE_E_ALIGN"
     assert append(cache(capacity=60), 0, 1) == "SAGE_E_SHAPE"   # capacity not a multiple of 8
+    # 2^20 blocks x 64 heads: 2^24 work-groups of 256 threads, one past the dispatch limit
+    assert append(cache(Hkv=64, capacity=1 << 23), 0, 1 << 23) == "SAGE_E_SHAPE"
     assert append(cache(), 0, 1, SageView(A, 0, 512, 256, 2)) == "SAGE_E_STRIDE"
     # a cache holds BF16 V or INT8 V (v8 with its scales), never both or neither
     assert append(cache(v=0), 0, 1) == "SAGE_E_NULL"

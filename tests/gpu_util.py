@@ -8,7 +8,7 @@ import sys
 import numpy as np
 import torch
 
-# Tolerance on the BF16 attention output against the oracle (spec bar).
+# Tolerance on the BF16 attention output against the oracle: max-abs and cosine.
 MAX_ABS = 2e-2
 MIN_COS = 0.999
 
